@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of grouped-query attention with per-head sinks on one MI355X.
+
+One step = split-KV decode (split pass + log-sum-exp merge) of the batched
+gpt-oss-shaped decode workload: 32 sequences x 1 query token over 4096 cached
+keys, 64 query heads on 8 KV heads, head_dim 64, bf16, 8 KV chunks per
+sequence.  `value` is the K/V bytes that step reads (268,435,456 B) divided by
+the step time, in GB/s; inputs are resident in HBM before timing starts and
+the timed steps rotate over several copies of K/V (>= 1 GiB in total) so the
+256 MB last-level cache cannot serve repeats.
+
+The same JSON line carries the prefill half of the metric (causal prefill,
+4 x 4096 tokens, 64/8 heads, bf16) as achieved TFLOP/s over the causal pairs,
+the roofline of the dominant kernel (timed with HIP events on the stream it
+runs on) and the fp64 CPU oracle timed on the host on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "decode KV GB/s (% HBM peak); prefill TFLOP/s (% bf16 MFMA peak)"
+KV_COPIES = 5                  # 5 x 268 MB rotated
+
+
+def _sync():
+    import torch
+    if torch.distributed.is_available() and torch.distributed.is_initialized():
+        torch.distributed.barrier()
+    torch.cuda.synchronize()
+
+
+def bench_decode(steps: int, warmup: int):
+    import torch
+    import gqa_attention_head_amd as sa
+    from gqa_attention_head_amd import workloads as W
+
+    wl = W.batched_decode()
+    dev = torch.device("cuda", 0)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q = up(wl.q16)
+    k0, v0 = up(wl.k16), up(wl.v16)
+    ks = [k0] + [k0.clone() for _ in range(KV_COPIES - 1)]
+    vs = [v0] + [v0.clone() for _ in range(KV_COPIES - 1)]
+    sinks = torch.from_numpy(wl.sinks).to(dev)
+    cu_k = torch.from_numpy(wl.cu_k).to(dev)
+    max_lk = int(wl.seqlens_k.max())
+    chunk = wl.kv_chunk
+    nch = -(-max_lk // chunk)
+    parts = sa.partial_buffers(wl.batch, wl.num_q_heads, nch, wl.head_dim, dev)
+    out = torch.empty(wl.batch, wl.num_q_heads, wl.head_dim, device=dev, dtype=torch.bfloat16)
+    lse = torch.empty(wl.batch, wl.num_q_heads, device=dev, dtype=torch.float32)
+
+    def step(i, ev=None):
+        j = i % KV_COPIES
+        if ev is not None:
+            ev[0].record()
+        sa.decode_split(q, ks[j], vs[j], sinks, cu_k, max_lk, chunk, nch, wl.sm_scale,
+                        partials=parts)
+        if ev is not None:
+            ev[1].record()
+        sa.merge(*parts, cu_k, chunk, out=out, lse=lse)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(warmup):
+        step(i)
+    _sync()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, evs[i])
+    _sync()
+    wall = time.perf_counter() - t0
+    split_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    merge_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
+    # untimed-by-events pass for the step time (no events between the launches)
+    _sync()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    _sync()
+    wall2 = time.perf_counter() - t0
+    kv_bytes = wl.kv_bytes()
+    ms_per_step = wall2 * 1e3 / steps
+    return dict(
+        workload=wl.name, kv_bytes=kv_bytes, ms_per_step=ms_per_step,
+        gbs=kv_bytes / (ms_per_step * 1e-3) / 1e9,
+        split_ms_mean=float(split_ms.mean()), split_ms_median=float(np.median(split_ms)),
+        merge_ms_mean=float(merge_ms.mean()), event_step_ms_mean=float(step_ms.mean()),
+        wall_ms_with_events=wall * 1e3 / steps, batch=wl.batch, kv_len=int(max_lk), chunk=chunk,
+        num_chunks=nch, wl=wl)
+
+
+def bench_prefill(steps: int, warmup: int):
+    import torch
+    import gqa_attention_head_amd as sa
+    from gqa_attention_head_amd import workloads as W
+
+    wl = W.causal_prefill()
+    dev = torch.device("cuda", 0)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, k, v = up(wl.q16), up(wl.k16), up(wl.v16)
+    sinks = torch.from_numpy(wl.sinks).to(dev)
+    cu_q = torch.from_numpy(wl.cu_q).to(dev)
+    cu_k = torch.from_numpy(wl.cu_k).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[0], q.shape[1], device=dev, dtype=torch.float32)
+    lq = int(wl.seqlens_q.max())
+
+    def step():
+        sa.prefill(q, k, v, sinks, cu_q, cu_k, lq, lq, wl.sm_scale, causal=True, out=out, lse=lse)
+
+    for _ in range(warmup):
+        step()
+    _sync()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        step()
+        evs[i][1].record()
+    _sync()
+    ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    flops = wl.prefill_flops()
+    mean_ms = float(ms.mean())
+    return dict(workload=wl.name, flops=flops, ms_mean=mean_ms, ms_median=float(np.median(ms)),
+                tflops=flops / (mean_ms * 1e-3) / 1e12, wl=wl)
+
+
+def cpu_baseline(dec_wl, pre_wl, budget_s: float = 20.0):
+    """The fp64 oracle, untuned, on the host: decode over whole sequences of the decode
+    workload, prefill over sampled query rows of the prefill workload."""
+    import oracle
+    orc = oracle.default()
+    threads = min(16, os.cpu_count() or 1)
+    # decode: the first 8 of 32 sequences (all 64 heads, all 4096 keys each)
+    nseq = 8
+    sub_rows = np.arange(nseq, dtype=np.int64)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        orc.workload(dec_wl, rows=sub_rows, nthreads=threads)
+        reps += 1
+        if time.perf_counter() - t0 > budget_s / 2:
+            break
+    dec_s = (time.perf_counter() - t0) / reps
+    dec_bytes = int(dec_wl.seqlens_k[:nseq].sum()) * dec_wl.num_kv_heads * dec_wl.head_dim * 2 * 2
+    # prefill: 16 rows from the end of each sequence (the longest rows), all heads
+    rows = np.concatenate([np.arange(int(pre_wl.cu_q[b + 1]) - 16, int(pre_wl.cu_q[b + 1]))
+                           for b in range(pre_wl.batch)]).astype(np.int64)
+    t0 = time.perf_counter()
+    orc.workload(pre_wl, rows=rows, nthreads=threads)
+    pre_s = time.perf_counter() - t0
+    pairs = 0
+    for r in rows:
+        b = int(np.searchsorted(pre_wl.cu_q, r, side="right") - 1)
+        i = int(r - pre_wl.cu_q[b])
+        pairs += int(pre_wl.seqlens_k[b]) - int(pre_wl.seqlens_q[b]) + i + 1
+    pre_flops = 4 * pre_wl.head_dim * pre_wl.num_q_heads * pairs
+    return dict(
+        value=dec_bytes / dec_s / 1e9, unit="GB/s", cores=threads, kind="oracle",
+        sample=f"decode: {nseq} of {dec_wl.batch} sequences x 64 heads x 4096 keys "
+               f"({dec_bytes} B of K/V), {reps} run(s), {dec_s:.3f} s each",
+        prefill=dict(value=pre_flops / pre_s / 1e12, unit="TFLOP/s",
+                     sample=f"prefill: {rows.size} query rows (last 16 of each sequence) x 64 heads, "
+                            f"{pre_s:.3f} s"))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this attention path has no multi-GPU leg.", file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+
+    dec = bench_decode(args.steps, args.warmup)
+    pre = None if args.no_prefill else bench_prefill(args.prefill_steps, max(2, args.warmup // 5))
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(dec["wl"], pre["wl"] if pre else __import__(
+            "gqa_attention_head_amd.workloads", fromlist=["x"]).causal_prefill())
+
+    split_gbs = dec["kv_bytes"] / (dec["split_ms_mean"] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(dec["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": dec["workload"], "batch": dec["batch"], "kv_len": dec["kv_len"],
+                   "num_q_heads": 64, "num_kv_heads": 8, "head_dim": 64,
+                   "kv_chunk": dec["chunk"], "num_chunks": dec["num_chunks"],
+                   "kv_copies_rotated": KV_COPIES, "parallelism": "single-gpu"},
+        "hbm_frac": round(dec["gbs"] / HBM_PEAK_GBS, 4),
+        "decode_kernels_ms": {"split_mean": round(dec["split_ms_mean"], 5),
+                              "merge_mean": round(dec["merge_ms_mean"], 5)},
+        "roofline": {"kernel": "decode_split_mfma<8>", "bound": "hbm",
+                     "achieved": round(split_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if pre is not None:
+        line["prefill"] = {
+            "workload": pre["workload"], "value": round(pre["tflops"], 2), "unit": "TFLOP/s",
+            "ms": round(pre["ms_mean"], 4), "flops": pre["flops"],
+            "roofline": {"kernel": "prefill_mfma<8>", "bound": "mfma",
+                         "achieved": round(pre["tflops"], 2), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(pre["tflops"] / BF16_PEAK_TFLOPS, 4),
+                         "traffic": None}}
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,202 @@
+"""Grouped-query attention with a learned per-head sink on MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libsinkattn.so`` (declared in
+``include/sink_attn.h``): it only checks and marshals torch tensors (device
+pointers, the current HIP stream) and maps status codes to exceptions.  Every
+step of the computation runs in the library's HIP kernels; there is no
+fallback.  If the library has not been built the calls raise.
+
+Operation ("GPT-OSS on day 0", Perplexity, Kernels for GPT-OSS / Sink
+attention): attn = softmax(q k^T * sm_scale + sink) V with one sink logit per
+query head acting as an extra softmax entry with a zero value vector.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG, "libsinkattn.so")
+
+SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_ELAUNCH = 0, 1, 2, 3
+SA_FP32, SA_BF16 = 0, 1
+EXPORTS = ("sink_attn_prefill", "sink_attn_decode_split", "sink_attn_merge",
+           "sink_attn_last_error")
+
+
+class SinkAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[status {status}] {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.environ.get("SINK_ATTN_LIBRARY", LIBRARY)
+
+
+def load_library():
+    """Load libsinkattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with gqa_attention_head_amd.build.build() "
+                           "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    lib.sink_attn_prefill.restype = ctypes.c_int
+    lib.sink_attn_prefill.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                      i32, i32, f32, i32, vp, vp, vp]
+    lib.sink_attn_decode_split.restype = ctypes.c_int
+    lib.sink_attn_decode_split.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                           i32, i32, i32, f32, vp, vp, vp, vp]
+    lib.sink_attn_merge.restype = ctypes.c_int
+    lib.sink_attn_merge.argtypes = [ctypes.c_int, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp,
+                                    vp, vp]
+    lib.sink_attn_last_error.restype = ctypes.c_char_p
+    lib.sink_attn_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != SA_OK:
+        msg = load_library().sink_attn_last_error().decode(errors="replace")
+        raise SinkAttnError(status, msg)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SA_BF16
+    if t.dtype == torch.float32:
+        return SA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, sm_scale,
+            causal=True, out=None, lse=None, return_lse=False, stream=None):
+    """Attention with sinks over a packed varlen batch; see ``sink_attn_prefill``.
+
+    q: [total_q, Hq, D]; k, v: [total_k, Hkv, D] (bf16 or fp32, same dtype);
+    sinks: [Hq] fp32; cu_seqlens_*: [B+1] int32.  Returns out (and lse [total_q, Hq]).
+    """
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name, q.dtype)
+    _dev(sinks, "sinks", torch.float32)
+    _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or k.shape != v.shape:
+        raise ValueError("q must be [total_q, Hq, D]; k and v [total_k, Hkv, D]")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    if lse is None and return_lse:
+        lse = torch.empty(q.shape[0], q.shape[1], device=q.device, dtype=torch.float32)
+    _dev(lse, "lse", torch.float32)
+    _check(lib.sink_attn_prefill(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(sinks),
+                                 _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), cu_seqlens_q.numel() - 1,
+                                 q.shape[1], k.shape[1], q.shape[2], int(max_seqlen_q),
+                                 int(max_seqlen_k), float(sm_scale), int(bool(causal)), _ptr(out),
+                                 _ptr(lse), _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def partial_buffers(batch, num_q_heads, max_num_chunks, head_dim=64, device="cuda"):
+    """Allocate (part_m, part_d, part_acc) for ``decode_split``."""
+    torch = _torch()
+    f = dict(device=device, dtype=torch.float32)
+    return (torch.empty(batch, num_q_heads, max_num_chunks, **f),
+            torch.empty(batch, num_q_heads, max_num_chunks, **f),
+            torch.empty(batch, num_q_heads, max_num_chunks, head_dim, **f))
+
+
+def decode_split(q, k, v, sinks, cu_seqlens_k, max_seqlen_k, kv_chunk_size, max_num_chunks,
+                 sm_scale, partials=None, stream=None):
+    """Split-KV decode first pass; returns (part_m, part_d, part_acc)."""
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name, q.dtype)
+    _dev(sinks, "sinks", torch.float32)
+    _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32)
+    batch = cu_seqlens_k.numel() - 1
+    if q.dim() != 3 or q.shape[0] != batch:
+        raise ValueError("q must be [batch, Hq, D] with batch = len(cu_seqlens_k) - 1")
+    if partials is None:
+        partials = partial_buffers(batch, q.shape[1], int(max_num_chunks), q.shape[2], q.device)
+    pm, pd, pa = partials
+    for name, t in (("part_m", pm), ("part_d", pd), ("part_acc", pa)):
+        _dev(t, name, torch.float32)
+    _check(lib.sink_attn_decode_split(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(sinks),
+                                      _ptr(cu_seqlens_k), batch, q.shape[1], k.shape[1],
+                                      q.shape[2], int(max_seqlen_k), int(kv_chunk_size),
+                                      int(max_num_chunks), float(sm_scale), _ptr(pm), _ptr(pd),
+                                      _ptr(pa), _stream(stream)))
+    return pm, pd, pa
+
+
+def merge(part_m, part_d, part_acc, cu_seqlens_k, kv_chunk_size, out_dtype=None, out=None,
+          lse=None, return_lse=False, stream=None):
+    """LSE combination of ``decode_split`` partials; returns out [B, Hq, D] (and lse)."""
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("part_m", part_m), ("part_d", part_d), ("part_acc", part_acc)):
+        _dev(t, name, torch.float32)
+    _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32)
+    batch, hq, max_num_chunks = part_m.shape
+    d = part_acc.shape[-1]
+    if out is None:
+        out = torch.empty(batch, hq, d, device=part_m.device, dtype=out_dtype or torch.bfloat16)
+    _dev(out, "out")
+    if lse is None and return_lse:
+        lse = torch.empty(batch, hq, device=part_m.device, dtype=torch.float32)
+    _dev(lse, "lse", torch.float32)
+    _check(lib.sink_attn_merge(_dtype_code(out), _ptr(part_m), _ptr(part_d), _ptr(part_acc),
+                               _ptr(cu_seqlens_k), int(kv_chunk_size), int(max_num_chunks), batch,
+                               hq, d, _ptr(out), _ptr(lse), _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def decode(q, k, v, sinks, cu_seqlens_k, max_seqlen_k, kv_chunk_size, sm_scale,
+           max_num_chunks=None, partials=None, out=None, lse=None, return_lse=False, stream=None):
+    """Split-KV decode: ``decode_split`` then ``merge`` on the same stream."""
+    if max_num_chunks is None:
+        max_num_chunks = max(1, -(-int(max_seqlen_k) // int(kv_chunk_size)))
+    pm, pd, pa = decode_split(q, k, v, sinks, cu_seqlens_k, max_seqlen_k, kv_chunk_size,
+                              max_num_chunks, sm_scale, partials=partials, stream=stream)
+    return merge(pm, pd, pa, cu_seqlens_k, kv_chunk_size, out_dtype=q.dtype, out=out, lse=lse,
+                 return_lse=return_lse, stream=stream)

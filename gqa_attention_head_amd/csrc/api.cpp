@@ -1,0 +1,172 @@
+// C ABI of the library: argument validation, kernel selection and launch.
+// Every check that needs only host data happens before anything is launched.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "kernels.h"
+#include "sink_attn.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sa_status_t fail(sa_status_t status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+sa_status_t ok() {
+    g_last_error.clear();
+    return SA_OK;
+}
+
+bool debug_sync() {
+    static const bool on = [] {
+        const char* e = std::getenv("SINK_ATTN_DEBUG");
+        return e != nullptr && e[0] == '1';
+    }();
+    return on;
+}
+
+sa_status_t check_device() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(SA_ELAUNCH, "no HIP device available: %s", hipGetErrorString(e));
+    }
+    return SA_OK;
+}
+
+sa_status_t finish_launch(hipError_t e, hipStream_t stream, const char* what) {
+    if (e != hipSuccess) return fail(SA_ELAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+    if (debug_sync()) {
+        e = hipStreamSynchronize(stream);
+        if (e != hipSuccess)
+            return fail(SA_ELAUNCH, "%s: kernel failed: %s", what, hipGetErrorString(e));
+    }
+    return ok();
+}
+
+sa_status_t check_heads(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim) {
+    if (batch < 1 || batch > 65535) return fail(SA_EINVAL, "batch must be in [1, 65535], got %d", batch);
+    if (hq < 1 || hkv < 1) return fail(SA_EINVAL, "head counts must be >= 1 (Hq=%d, Hkv=%d)", hq, hkv);
+    if (hq % hkv != 0) return fail(SA_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", hq, hkv);
+    if (hkv > 65535) return fail(SA_EINVAL, "Hkv must be <= 65535, got %d", hkv);
+    if (hq / hkv > 64) return fail(SA_EUNSUPPORTED, "group size Hq/Hkv = %d > 64 is not supported", hq / hkv);
+    if (head_dim != 64) return fail(SA_EUNSUPPORTED, "head_dim %d is not supported (only 64)", head_dim);
+    return SA_OK;
+}
+
+sa_status_t check_dtype(sa_dtype_t d) {
+    if (d != SA_FP32 && d != SA_BF16) return fail(SA_EINVAL, "unknown dtype %d", (int)d);
+    return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sink_attn_last_error(void) { return g_last_error.c_str(); }
+
+sa_status_t sink_attn_prefill(sa_dtype_t dtype, const void* q, const void* k, const void* v,
+                              const float* sinks, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, int32_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen_q,
+                              int32_t max_seqlen_k, float sm_scale, int32_t causal, void* out,
+                              float* lse, void* stream) {
+    sa_status_t s;
+    if ((s = check_dtype(dtype)) != SA_OK) return s;
+    if (!q || !k || !v || !sinks || !cu_seqlens_q || !cu_seqlens_k || !out)
+        return fail(SA_EINVAL, "sink_attn_prefill: null pointer argument");
+    if ((s = check_heads(batch, num_q_heads, num_kv_heads, head_dim)) != SA_OK) return s;
+    if (max_seqlen_q < 0 || max_seqlen_k < 0)
+        return fail(SA_EINVAL, "max_seqlen_q/max_seqlen_k must be >= 0");
+    if (causal != 0 && causal != 1) return fail(SA_EINVAL, "causal must be 0 or 1");
+    if (!std::isfinite(sm_scale)) return fail(SA_EINVAL, "sm_scale must be finite");
+    if (max_seqlen_q == 0) return ok();
+    if ((s = check_device()) != SA_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int group = num_q_heads / num_kv_heads;
+    hipError_t e;
+    if (dtype == SA_BF16 && sa::mfma_prefill_supported(group))
+        e = sa::launch_mfma_prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, batch, num_q_heads,
+                                    num_kv_heads, max_seqlen_q, sm_scale, causal, out, lse, st);
+    else
+        e = sa::launch_generic_prefill(dtype == SA_BF16, q, k, v, sinks, cu_seqlens_q,
+                                       cu_seqlens_k, batch, num_q_heads, num_kv_heads,
+                                       max_seqlen_q, sm_scale, causal, out, lse, st);
+    return finish_launch(e, st, "sink_attn_prefill");
+}
+
+sa_status_t sink_attn_decode_split(sa_dtype_t dtype, const void* q, const void* k, const void* v,
+                                   const float* sinks, const int32_t* cu_seqlens_k, int32_t batch,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t max_seqlen_k, int32_t kv_chunk_size,
+                                   int32_t max_num_chunks, float sm_scale, float* part_m,
+                                   float* part_d, float* part_acc, void* stream) {
+    sa_status_t s;
+    if ((s = check_dtype(dtype)) != SA_OK) return s;
+    if (!q || !k || !v || !sinks || !cu_seqlens_k || !part_m || !part_d || !part_acc)
+        return fail(SA_EINVAL, "sink_attn_decode_split: null pointer argument");
+    if ((s = check_heads(batch, num_q_heads, num_kv_heads, head_dim)) != SA_OK) return s;
+    if (kv_chunk_size < 1) return fail(SA_EINVAL, "kv_chunk_size must be >= 1, got %d", kv_chunk_size);
+    if (max_seqlen_k < 0) return fail(SA_EINVAL, "max_seqlen_k must be >= 0");
+    const int64_t need = max_seqlen_k == 0 ? 1 : ((int64_t)max_seqlen_k + kv_chunk_size - 1) / kv_chunk_size;
+    if (max_num_chunks < need)
+        return fail(SA_EINVAL, "max_num_chunks (%d) < ceil(max_seqlen_k / kv_chunk_size) = %lld",
+                    max_num_chunks, (long long)need);
+    if (!std::isfinite(sm_scale)) return fail(SA_EINVAL, "sm_scale must be finite");
+    const int group = num_q_heads / num_kv_heads;
+    const bool mfma = dtype == SA_BF16 && sa::mfma_decode_supported(group);
+    if (mfma && (int64_t)batch * max_num_chunks * num_kv_heads > 0x7fffffffLL)
+        return fail(SA_EINVAL, "batch * max_num_chunks * Hkv exceeds the grid limit");
+    if (!mfma && max_num_chunks > 0x7fffffff) return fail(SA_EINVAL, "max_num_chunks too large");
+    if ((s = check_device()) != SA_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (mfma)
+        e = sa::launch_mfma_decode_split(q, k, v, sinks, cu_seqlens_k, batch, num_q_heads,
+                                         num_kv_heads, kv_chunk_size, max_num_chunks, sm_scale,
+                                         part_m, part_d, part_acc, st);
+    else
+        e = sa::launch_generic_decode_split(dtype == SA_BF16, q, k, v, sinks, cu_seqlens_k, batch,
+                                            num_q_heads, num_kv_heads, kv_chunk_size,
+                                            max_num_chunks, sm_scale, part_m, part_d, part_acc, st);
+    return finish_launch(e, st, "sink_attn_decode_split");
+}
+
+sa_status_t sink_attn_merge(sa_dtype_t out_dtype, const float* part_m, const float* part_d,
+                            const float* part_acc, const int32_t* cu_seqlens_k,
+                            int32_t kv_chunk_size, int32_t max_num_chunks, int32_t batch,
+                            int32_t num_q_heads, int32_t head_dim, void* out, float* lse,
+                            void* stream) {
+    sa_status_t s;
+    if ((s = check_dtype(out_dtype)) != SA_OK) return s;
+    if (!part_m || !part_d || !part_acc || !cu_seqlens_k || !out)
+        return fail(SA_EINVAL, "sink_attn_merge: null pointer argument");
+    if (batch < 1 || batch > 65535) return fail(SA_EINVAL, "batch must be in [1, 65535], got %d", batch);
+    if (num_q_heads < 1) return fail(SA_EINVAL, "num_q_heads must be >= 1");
+    if ((int64_t)batch * num_q_heads > 0x7fffffffLL)
+        return fail(SA_EINVAL, "batch * num_q_heads exceeds the grid limit");
+    if (head_dim != 64) return fail(SA_EUNSUPPORTED, "head_dim %d is not supported (only 64)", head_dim);
+    if (kv_chunk_size < 1) return fail(SA_EINVAL, "kv_chunk_size must be >= 1, got %d", kv_chunk_size);
+    if (max_num_chunks < 1) return fail(SA_EINVAL, "max_num_chunks must be >= 1");
+    if ((s = check_device()) != SA_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = sa::launch_merge(out_dtype == SA_BF16, part_m, part_d, part_acc, cu_seqlens_k,
+                                    kv_chunk_size, max_num_chunks, batch, num_q_heads, out, lse, st);
+    return finish_launch(e, st, "sink_attn_merge");
+}
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+// Vector-ALU kernel, float32 arithmetic; any group size G = hq / hkv <= 64, head_dim 64.
+hipError_t launch_generic_prefill(bool bf16, const void* q, const void* k, const void* v,
+                                  const float* sinks, const int32_t* cu_q, const int32_t* cu_k,
+                                  int batch, int hq, int hkv, int max_lq, float sm_scale,
+                                  int causal, void* out, float* lse, hipStream_t stream);
+hipError_t launch_generic_decode_split(bool bf16, const void* q, const void* k, const void* v,
+                                       const float* sinks, const int32_t* cu_k, int batch, int hq,
+                                       int hkv, int chunk, int max_chunks, float sm_scale,
+                                       float* part_m, float* part_d, float* part_acc,
+                                       hipStream_t stream);
+
+// bf16 matrix-core kernels, head_dim 64.
+bool mfma_decode_supported(int group);
+hipError_t launch_mfma_decode_split(const void* q, const void* k, const void* v,
+                                    const float* sinks, const int32_t* cu_k, int batch, int hq,
+                                    int hkv, int chunk, int max_chunks, float sm_scale,
+                                    float* part_m, float* part_d, float* part_acc,
+                                    hipStream_t stream);
+bool mfma_prefill_supported(int group);
+hipError_t launch_mfma_prefill(const void* q, const void* k, const void* v, const float* sinks,
+                               const int32_t* cu_q, const int32_t* cu_k, int batch, int hq,
+                               int hkv, int max_lq, float sm_scale, int causal, void* out,
+                               float* lse, hipStream_t stream);
+
+// Log-sum-exp combination of split-KV chunk states.
+hipError_t launch_merge(bool out_bf16, const float* part_m, const float* part_d,
+                        const float* part_acc, const int32_t* cu_k, int chunk, int max_chunks,
+                        int batch, int hq, void* out, float* lse, hipStream_t stream);
+
+}  // namespace sa

@@ -1,0 +1,244 @@
+// Attention with a per-head sink over a packed varlen batch (prefill), bf16
+// inputs, head_dim 64, matrix cores (gfx950).
+//
+// "GPT-OSS on day 0" (Perplexity), Kernels for GPT-OSS / Sink attention: the
+// softmax is computed online with the maximum subtracted, the running maximum m
+// starting at the head's sink and the running scale d at 1; the same kernel
+// family serves prefill and decode.  The whole KV range of a query block is
+// one block here, so the sink enters the state once, at the start.
+//
+// Work decomposition.  One workgroup per (sequence b, KV head g, 32-row query
+// block); wave w of the workgroup handles query head g*G + w, so the G query
+// heads that share KV head g (grouped-query attention) share every K/V tile
+// the workgroup stages in LDS.  Query blocks are issued heaviest first (the
+// causal triangle gives late blocks the most keys).
+//
+// Per 64-key tile and wave (scores kept transposed, S^T = K Q^T, so that the
+// exponentiated tile is already laid out as the B operand of the PV product):
+//   S^T[64 keys x 32 rows] = K[64 x 64] . Q^T[64 x 32]      8 MFMA 32x32x16
+//   bottom-right causal mask on diagonal tiles, online softmax in base 2
+//   O^T[64 dims x 32 rows] += V^T[64 x 64] . P^T[64 x 32]   8 MFMA 32x32x16
+//     (V read transposed out of LDS with ds_read_b64_tr_b16)
+// K/V tiles are double-buffered: the next tile's global loads are in flight
+// while the current tile is computed.
+#include "common.h"
+#include "kernels.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int kD = 64;
+constexpr int kBQ = 32;             // query rows per wave
+constexpr int kBK = 64;             // keys per tile
+constexpr int kStride = kD + 8;     // LDS row stride in bf16 elements (144 bytes)
+constexpr int kSegs = kBK * kD / 8; // 16-byte segments per K (or V) tile
+
+template <int G>
+__global__ __launch_bounds__(64 * G) void prefill_mfma(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ sinks,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int hq, int hkv,
+    int n_qblocks, float scale_log2, int causal, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
+    constexpr int kThreads = 64 * G;
+    constexpr int kPer = (kSegs + kThreads - 1) / kThreads;
+    __shared__ uint16_t kl[2][kBK * kStride];
+    __shared__ uint16_t vl[2][kBK * kStride];
+
+    const int qb = n_qblocks - 1 - (int)blockIdx.x;  // heaviest blocks first
+    const int g = blockIdx.y, b = blockIdx.z;
+    const int q0 = cu_q[b], lq = cu_q[b + 1] - q0;
+    const int k0 = cu_k[b], lk = cu_k[b + 1] - k0;
+    const int r0 = qb * kBQ;
+    if (r0 >= lq) return;  // uniform over the workgroup
+
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int h = g * G + wave;
+    const int l32 = lane % 32, half = lane / 32;
+    const int row = r0 + l32;
+    const bool row_ok = row < lq;
+    const int last = min(r0 + kBQ, lq) - 1;
+    // keys [0, kend) are visible to some row of the block; [0, full_end) to every row.
+    const int kend = causal ? max(0, min(lk, lk - lq + last + 1)) : lk;
+    const int full_end = causal ? max(0, min(lk, lk - lq + r0 + 1)) : lk;
+    const int row_lim = causal ? min(lk, lk - lq + row + 1) : lk;
+
+    // B operand of S^T = K Q^T: lane holds Q[row][16*ks + 8*half .. +7].
+    bf16x8 qop[4];
+    {
+        const uint16_t* qp = q + ((int64_t)(q0 + min(row, lq - 1)) * hq + h) * kD + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qop[ks] = load_bf16x8(qp + 16 * ks);
+    }
+
+    float m = sinks[h] * kLog2e;          // running max starts at the sink (base-2 units)
+    float dl = (half == 0) ? 1.0f : 0.0f; // running scale, split over the two lane halves
+    f32x16 o[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[mt][i] = 0.0f;
+
+    const int row_stride = hkv * kD;
+    const uint16_t* kbase = k + ((int64_t)k0 * hkv + g) * kD;
+    const uint16_t* vbase = v + ((int64_t)k0 * hkv + g) * kD;
+    u32x4 kreg[kPer], vreg[kPer];
+    auto gload = [&](int j0) {
+#pragma unroll
+        for (int p = 0; p < kPer; ++p) {
+            const int idx = threadIdx.x + p * kThreads;
+            if (kSegs % kThreads == 0 || idx < kSegs) {
+                const int key = min(j0 + idx / 8, lk - 1);
+                const int64_t off = (int64_t)key * row_stride + 8 * (idx % 8);
+                kreg[p] = *reinterpret_cast<const u32x4*>(kbase + off);
+                vreg[p] = *reinterpret_cast<const u32x4*>(vbase + off);
+            }
+        }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < kPer; ++p) {
+            const int idx = threadIdx.x + p * kThreads;
+            if (kSegs % kThreads == 0 || idx < kSegs) {
+                const int off = (idx / 8) * kStride + 8 * (idx % 8);
+                *reinterpret_cast<u32x4*>(&kl[buf][off]) = kreg[p];
+                *reinterpret_cast<u32x4*>(&vl[buf][off]) = vreg[p];
+            }
+        }
+    };
+
+    const int ntiles = ceil_div(kend, kBK);
+    if (ntiles > 0) {
+        gload(0);
+        lstore(0);
+    }
+    __syncthreads();
+    const int g4 = lane / 16, c16 = lane % 16;
+    for (int t = 0; t < ntiles; ++t) {
+        const int j0 = t * kBK;
+        const int buf = t & 1;
+        const bool more = t + 1 < ntiles;
+        if (more) gload(j0 + kBK);
+        const uint16_t* kt = kl[buf];
+        const uint16_t* vt = vl[buf];
+
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 a = load_bf16x8(kt + (32 * kb + l32) * kStride + 16 * ks + 8 * half);
+                s[kb] = mfma32x32x16(a, qop[ks], s[kb]);
+            }
+        }
+        // s[kb][i] = S^T[key j0 + 32*kb + 8*(i/4) + 4*half + i%4][row]
+        const bool need_mask = j0 + kBK > full_end;
+        float tmax = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float x = s[kb][i] * scale_log2;
+                if (need_mask) {
+                    const int key = j0 + 32 * kb + 8 * (i / 4) + 4 * half + (i % 4);
+                    if (key >= row_lim) x = kNegInf;
+                }
+                s[kb][i] = x;
+                tmax = fmaxf(tmax, x);
+            }
+        tmax = max_xor32(tmax);
+        const float m_new = fmaxf(m, tmax);
+        const bool live = m_new != kNegInf;
+        const float alpha = live ? fast_exp2(m - m_new) : 1.0f;
+        const float msub = live ? m_new : 0.0f;
+        float psum = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float p = fast_exp2(s[kb][i] - msub);
+                s[kb][i] = p;
+                psum += p;
+            }
+        dl = dl * alpha + psum;
+        m = m_new;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) o[mt] *= alpha;
+
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int kb = ks / 2, hs = ks % 2;
+            bf16x8 pb;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pb[i] = static_cast<__bf16>(s[kb][8 * hs + i]);
+            const int key_base = 32 * kb + 16 * hs;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const uint16_t* p0 = vt + (key_base + 4 * half + c16 / 4) * kStride + 32 * mt +
+                                     16 * (g4 % 2) + 4 * (c16 % 4);
+                const bf16x8 va = concat(lds_read_tr16(p0), lds_read_tr16(p0 + 8 * kStride));
+                o[mt] = mfma32x32x16(va, pb, o[mt]);
+            }
+        }
+        if (more) lstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    const float dsum = sum_xor32(dl);
+    if (!row_ok) return;
+    const int64_t orow = (int64_t)(q0 + row) * hq + h;
+    const bool empty = (m == kNegInf) || !(dsum > 0.0f);
+    const float inv = empty ? 0.0f : 1.0f / dsum;
+    uint16_t* op = out + orow * kD;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            // o[mt][4j + e] = O^T[dim 32*mt + 8*j + 4*half + e][row]
+            uint32_t lo = (uint32_t)f32_to_bf16_bits(o[mt][4 * j + 0] * inv) |
+                          ((uint32_t)f32_to_bf16_bits(o[mt][4 * j + 1] * inv) << 16);
+            uint32_t hi = (uint32_t)f32_to_bf16_bits(o[mt][4 * j + 2] * inv) |
+                          ((uint32_t)f32_to_bf16_bits(o[mt][4 * j + 3] * inv) << 16);
+            *reinterpret_cast<u32x2*>(op + 32 * mt + 8 * j + 4 * half) = u32x2{lo, hi};
+        }
+    if (lse != nullptr && half == 0)
+        lse[orow] = empty ? kNegInf : (m + fast_log2(dsum)) * kLn2;
+}
+
+template <int G>
+hipError_t launch_g(const void* q, const void* k, const void* v, const float* sinks,
+                    const int32_t* cu_q, const int32_t* cu_k, int batch, int hq, int hkv,
+                    int max_lq, float sm_scale, int causal, void* out, float* lse,
+                    hipStream_t stream) {
+    const int n_qblocks = ceil_div(max_lq, kBQ);
+    dim3 grid(n_qblocks, hkv, batch);
+    hipLaunchKernelGGL((prefill_mfma<G>), grid, dim3(64 * G), 0, stream, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, sinks, cu_q, cu_k, hq, hkv,
+                       n_qblocks, sm_scale * kLog2e, causal, (uint16_t*)out, lse);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool mfma_prefill_supported(int group) {
+    return group == 1 || group == 2 || group == 4 || group == 8 || group == 16;
+}
+
+hipError_t launch_mfma_prefill(const void* q, const void* k, const void* v, const float* sinks,
+                               const int32_t* cu_q, const int32_t* cu_k, int batch, int hq,
+                               int hkv, int max_lq, float sm_scale, int causal, void* out,
+                               float* lse, hipStream_t stream) {
+    switch (hq / hkv) {
+        case 1: return launch_g<1>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, stream);
+        case 2: return launch_g<2>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, stream);
+        case 4: return launch_g<4>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, stream);
+        case 8: return launch_g<8>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, stream);
+        case 16: return launch_g<16>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace sa

@@ -1,0 +1,142 @@
+/*
+ * sink_attn.h -- C ABI of the MI355X (gfx950) library for grouped-query
+ * attention with a learned per-head attention sink.
+ *
+ * The operation is the one described in "GPT-OSS on day 0" (Perplexity),
+ * section "Kernels for GPT-OSS / Sink attention":
+ *
+ *     attn = softmax(q k^T * sm_scale + sink) V
+ *
+ * where each query head h owns one pre-trained sink logit (section
+ * "Attention and MLP architecture": GQA with attention sinks; each head
+ * carries a sink parameter that enters its softmax).  The library reads the
+ * sink as one more softmax entry with a zero value vector: it is added to
+ * the denominator, it is NOT multiplied by sm_scale and it is in natural-log
+ * units.  That is what starting the online softmax's running maximum at the
+ * head's sink value (with the running scale at 1) computes, as the same
+ * section describes; when the keys are split into blocks along the sequence
+ * the sink enters the first block only.
+ *
+ * Grouped-query attention: with Hq query heads and Hkv key/value heads,
+ * query head h reads key/value head h / (Hq / Hkv).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer; arrays are contiguous and
+ *     row-major.  Token-major packed layout: q [total_q, Hq, D],
+ *     k and v [total_k, Hkv, D].  head_dim D = 64 is supported.
+ *   - cu_seqlens_* are device int32 arrays of batch+1 nondecreasing
+ *     absolute row offsets: sequence b owns rows [cu[b], cu[b+1]).
+ *   - The caller allocates and owns every buffer (including the split-KV
+ *     partial buffers).  The library never allocates, frees or synchronises.
+ *     Inputs are read-only; outputs must not alias inputs.
+ *   - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL is
+ *     the default stream).
+ *   - Host-checkable errors are reported before anything is launched:
+ *     SA_EINVAL for invalid arguments, SA_EUNSUPPORTED for a valid but
+ *     unimplemented combination (dtype, head_dim, group size), SA_ELAUNCH if
+ *     the HIP runtime rejects the launch or no device is present.  The text
+ *     of the last error of the calling thread is returned by
+ *     sink_attn_last_error().
+ *   - Device-resident preconditions cannot be checked without a
+ *     synchronisation and are the caller's duty: monotone cu_seqlens,
+ *     L_q <= L_k for every sequence under causal masking, per-sequence
+ *     lengths no larger than the max_seqlen_* bounds given, sinks that are
+ *     finite or -inf (never +inf or NaN).
+ */
+#ifndef SINK_ATTN_H
+#define SINK_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SA_OK = 0,
+    SA_EINVAL = 1,
+    SA_EUNSUPPORTED = 2,
+    SA_ELAUNCH = 3
+} sa_status_t;
+
+typedef enum {
+    SA_FP32 = 0,   /* IEEE float32 */
+    SA_BF16 = 1    /* bfloat16 (upper 16 bits of a float32), round-to-nearest-even on output */
+} sa_dtype_t;
+
+/*
+ * Attention with sinks over a packed varlen batch (prefill, or any mix of
+ * prefill chunks and single-token decodes).
+ *
+ * The section's operation for every query row: with L_q queries and L_k keys
+ * in sequence b, row i (0-based within the sequence) sees keys
+ * 0 .. L_k - L_q + i when `causal` is nonzero (bottom-right alignment: the
+ * row sits at key position L_k - L_q + i), and all L_k keys otherwise.
+ *
+ *   q      [total_q, Hq, D]   dtype
+ *   k, v   [total_k, Hkv, D]  dtype
+ *   sinks  [Hq] float32, natural-log units, finite or -inf
+ *   cu_seqlens_q, cu_seqlens_k  [batch+1] int32
+ *   max_seqlen_q, max_seqlen_k  host-side upper bounds of L_q and L_k (grid sizing)
+ *   out    [total_q, Hq, D]   dtype; rows with no visible key and sink = -inf get 0
+ *   lse    nullable; [total_q, Hq] float32: ln(e^sink + sum_j e^(s_j)), -inf if empty
+ */
+sa_status_t sink_attn_prefill(sa_dtype_t dtype, const void *q, const void *k, const void *v,
+                              const float *sinks, const int32_t *cu_seqlens_q,
+                              const int32_t *cu_seqlens_k, int32_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t max_seqlen_q,
+                              int32_t max_seqlen_k, float sm_scale, int32_t causal, void *out,
+                              float *lse, void *stream);
+
+/*
+ * Split-KV decode, first pass: one query token per sequence, the keys of each
+ * sequence cut into blocks ("chunks") along the sequence, as the section
+ * describes for attention parallelised along the KV length.  Chunk c of
+ * sequence b covers keys [c*C, min((c+1)*C, L_b)) with C = kv_chunk_size;
+ * nchunks(b) = max(1, ceil(L_b / C)) (chunk 0 always exists because it
+ * carries the sink).  The running maximum of chunk 0 starts at the head's
+ * sink, that of every other chunk at -inf; the running scale starts at 1.
+ *
+ *   q          [batch, Hq, D] dtype
+ *   k, v       [total_k, Hkv, D] dtype, sequence b's keys at rows [cu_seqlens_k[b], cu_seqlens_k[b+1])
+ *   max_seqlen_k  host-side upper bound of L_b
+ *   max_num_chunks  slots per (b, h) in the partial buffers; must be >= ceil(max_seqlen_k / C)
+ *   part_m, part_d  [batch, Hq, max_num_chunks] float32
+ *   part_acc        [batch, Hq, max_num_chunks, D] float32
+ * For every c < nchunks(b) the call writes the state after chunk c's keys:
+ * m (natural-log units), d = sum over the chunk of e^(s_j - m) (plus
+ * e^(sink - m) in chunk 0) and acc = sum of e^(s_j - m) v_j (unnormalised).
+ * A chunk whose state holds no mass has m = -inf.  Slots c >= nchunks(b) are
+ * not written.
+ */
+sa_status_t sink_attn_decode_split(sa_dtype_t dtype, const void *q, const void *k, const void *v,
+                                   const float *sinks, const int32_t *cu_seqlens_k, int32_t batch,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t max_seqlen_k, int32_t kv_chunk_size,
+                                   int32_t max_num_chunks, float sm_scale, float *part_m,
+                                   float *part_d, float *part_acc, void *stream);
+
+/*
+ * Split-KV decode, second pass: the log-sum-exp combination of the chunk
+ * states written by sink_attn_decode_split (same cu_seqlens_k, chunk size and
+ * max_num_chunks):  M = max_c m_c,  w_c = e^(m_c - M),
+ * out = sum_c w_c acc_c / sum_c w_c d_c,  lse = M + ln sum_c w_c d_c;
+ * out = 0 and lse = -inf when every chunk is at -inf.
+ *
+ *   out  [batch, Hq, D] out_dtype
+ *   lse  nullable; [batch, Hq] float32
+ */
+sa_status_t sink_attn_merge(sa_dtype_t out_dtype, const float *part_m, const float *part_d,
+                            const float *part_acc, const int32_t *cu_seqlens_k,
+                            int32_t kv_chunk_size, int32_t max_num_chunks, int32_t batch,
+                            int32_t num_q_heads, int32_t head_dim, void *out, float *lse,
+                            void *stream);
+
+/* Text of the calling thread's last non-OK status ("" if none).  Valid until the next call. */
+const char *sink_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SINK_ATTN_H */

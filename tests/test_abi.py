@@ -1,0 +1,159 @@
+"""C-ABI contract on the CPU: the library loads, exports what include/sink_attn.h
+declares, and rejects invalid arguments before launching anything."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+import gqa_attention_head_amd as sa
+from gqa_attention_head_amd import build as sa_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER_DIR = os.path.join(ROOT, "include")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sa.LIBRARY):
+        sa_build.build()
+    return sa.load_library()
+
+
+def declared_functions():
+    names = []
+    for fn in sorted(os.listdir(HEADER_DIR)):
+        if fn.endswith(".h"):
+            text = open(os.path.join(HEADER_DIR, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(sink_attn_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(sa.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", sa.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def _no_gpu():
+    try:
+        import torch
+        return not torch.cuda.is_available()
+    except Exception:
+        return True
+
+
+P = ctypes.c_void_p(256)  # never dereferenced: every call below fails validation first
+NULL = None
+
+
+def _prefill(lib, **kw):
+    a = dict(dtype=sa.SA_BF16, q=P, k=P, v=P, sinks=P, cu_q=P, cu_k=P, batch=2, hq=64, hkv=8,
+             d=64, max_q=16, max_k=16, scale=0.125, causal=1, out=P, lse=NULL, stream=NULL)
+    a.update(kw)
+    return lib.sink_attn_prefill(*a.values())
+
+
+def _split(lib, **kw):
+    a = dict(dtype=sa.SA_BF16, q=P, k=P, v=P, sinks=P, cu_k=P, batch=2, hq=64, hkv=8, d=64,
+             max_k=4096, chunk=512, max_chunks=8, scale=0.125, pm=P, pd=P, pa=P, stream=NULL)
+    a.update(kw)
+    return lib.sink_attn_decode_split(*a.values())
+
+
+def _merge(lib, **kw):
+    a = dict(dtype=sa.SA_BF16, pm=P, pd=P, pa=P, cu_k=P, chunk=512, max_chunks=8, batch=2,
+             hq=64, d=64, out=P, lse=NULL, stream=NULL)
+    a.update(kw)
+    return lib.sink_attn_merge(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), sa.SA_EINVAL),
+    (dict(out=NULL), sa.SA_EINVAL),
+    (dict(sinks=NULL), sa.SA_EINVAL),
+    (dict(batch=0), sa.SA_EINVAL),
+    (dict(hq=60, hkv=8), sa.SA_EINVAL),
+    (dict(hkv=0), sa.SA_EINVAL),
+    (dict(d=128), sa.SA_EUNSUPPORTED),
+    (dict(hq=128, hkv=1), sa.SA_EUNSUPPORTED),
+    (dict(dtype=7), sa.SA_EINVAL),
+    (dict(causal=2), sa.SA_EINVAL),
+    (dict(max_q=-1), sa.SA_EINVAL),
+    (dict(scale=float("nan")), sa.SA_EINVAL),
+])
+def test_prefill_rejects(lib, kw, status):
+    assert _prefill(lib, **kw) == status
+    assert lib.sink_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pa=NULL), sa.SA_EINVAL),
+    (dict(chunk=0), sa.SA_EINVAL),
+    (dict(max_chunks=7), sa.SA_EINVAL),       # ceil(4096 / 512) = 8 slots needed
+    (dict(max_k=-1), sa.SA_EINVAL),
+    (dict(hq=64, hkv=7), sa.SA_EINVAL),
+    (dict(d=32), sa.SA_EUNSUPPORTED),
+    (dict(scale=float("inf")), sa.SA_EINVAL),
+])
+def test_decode_split_rejects(lib, kw, status):
+    assert _split(lib, **kw) == status
+    assert lib.sink_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=NULL), sa.SA_EINVAL),
+    (dict(chunk=0), sa.SA_EINVAL),
+    (dict(max_chunks=0), sa.SA_EINVAL),
+    (dict(batch=0), sa.SA_EINVAL),
+    (dict(d=80), sa.SA_EUNSUPPORTED),
+])
+def test_merge_rejects(lib, kw, status):
+    assert _merge(lib, **kw) == status
+    assert lib.sink_attn_last_error().decode()
+
+
+def test_empty_prefill_is_a_no_op(lib):
+    assert _prefill(lib, max_q=0) == sa.SA_OK
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="needs a host without a GPU (would launch on fake pointers)")
+def test_valid_call_without_device_reports_launch_error(lib):
+    assert _prefill(lib) == sa.SA_ELAUNCH
+    assert "device" in lib.sink_attn_last_error().decode()
+    assert _split(lib) == sa.SA_ELAUNCH
+    assert _merge(lib) == sa.SA_ELAUNCH
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    code = ("import gqa_attention_head_amd as sa\n"
+            "try:\n    sa.load_library()\nexcept RuntimeError as e:\n    print('raised', e)\n")
+    env = dict(os.environ, SINK_ATTN_LIBRARY=str(tmp_path / "absent.so"), PYTHONPATH=ROOT)
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env)
+    assert "raised" in res.stdout
+
+
+def test_product_does_not_touch_the_oracle():
+    pkg = os.path.join(ROOT, "gqa_attention_head_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), fn
+                assert "oracle.c" not in text and "liboracle" not in text, fn
+    code = "import sys, gqa_attention_head_amd; print('oracle' in sys.modules)"
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         env=dict(os.environ, PYTHONPATH=ROOT), check=True)
+    assert res.stdout.strip() == "False"

@@ -1,0 +1,222 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Every comparison is element by element on the same seeded inputs; bf16 paths
+to max-abs 2e-2 / mean-abs 2e-3, fp32 paths to max-abs 1e-5.  Full-size
+workloads are compared on every output where the oracle finishes in seconds,
+otherwise on sampled query rows (each computed by the oracle on its own).
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from gqa_attention_head_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - collected on CPU hosts too
+    pytest.skip("no GPU", allow_module_level=True)
+
+import gpu_helpers as H  # noqa: E402
+
+NTHREADS = min(16, os.cpu_count() or 1)
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+def _sample_rows(wl, per_seq=24, seed=0):
+    """Rows at tile edges, the first and last rows, and random rows of every sequence."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for b in range(wl.batch):
+        lo, lq = int(wl.cu_q[b]), int(wl.seqlens_q[b])
+        fixed = {0, 1, 31, 32, 33, 63, 64, 65, lq // 2, lq - 2, lq - 1}
+        cand = sorted(x for x in fixed if 0 <= x < lq)
+        extra = rng.choice(lq, size=min(per_seq, lq), replace=False).tolist() if lq else []
+        rows += [lo + x for x in sorted(set(cand) | set(extra))]
+    return np.array(rows, dtype=np.int64)
+
+
+# ---------------------------------------------------------------- the five workloads
+
+def test_tiny_prefill_fp32(orc):
+    wl = W.workload(1)
+    dev = H.Device(wl)
+    out, lse = H.run_prefill(dev)
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    H.assert_close(out, ref, bf16=False)
+    H.assert_lse_close(lse, ref_lse, bf16=False)
+
+
+def test_batched_decode_split8(orc):
+    wl = W.workload(2)
+    dev = H.Device(wl)
+    out, lse, pm, pd, pa = H.run_decode(dev, wl.kv_chunk, return_partials=True)
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    H.assert_close(out, ref[:, :, :], bf16=True)
+    H.assert_lse_close(lse, ref_lse, bf16=True)
+    # chunk states (m, d, acc): compare what is unique, acc/d and m + ln d
+    nch = pm.shape[2]
+    om, od, oa = orc.partials(wl.q32, wl.k32, wl.v32, wl.sinks, wl.cu_k, wl.sm_scale,
+                              wl.kv_chunk, nch, nthreads=NTHREADS)
+    H.assert_close(pa / pd[..., None], oa / od[..., None], bf16=True, what="chunk acc/d")
+    np.testing.assert_allclose(pm + np.log(pd), om + np.log(od), atol=H.BF16_LSE)
+
+
+def test_causal_prefill_4x4096_sampled(orc):
+    wl = W.workload(3)
+    dev = H.Device(wl)
+    out, lse = H.run_prefill(dev)
+    rows = _sample_rows(wl, per_seq=24)
+    ref, ref_lse = orc.workload(wl, rows=rows, nthreads=NTHREADS)
+    H.assert_close(out[rows], ref, bf16=True)
+    H.assert_lse_close(lse[rows], ref_lse, bf16=True)
+    assert np.all(np.isfinite(out))
+
+
+def test_ragged_long_decode(orc):
+    wl = W.workload(4)
+    dev = H.Device(wl)
+    out, lse = H.run_decode(dev, wl.kv_chunk)
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    H.assert_close(out, ref, bf16=True)
+    H.assert_lse_close(lse, ref_lse, bf16=True)
+
+
+@pytest.mark.parametrize("permute", [False, True])
+def test_mixed_varlen_prefill_call(orc, permute):
+    wl = W.mixed_varlen(permute=permute)
+    dev = H.Device(wl)
+    out, lse = H.run_prefill(dev)
+    rows = _sample_rows(wl, per_seq=16)
+    ref, ref_lse = orc.workload(wl, rows=rows, nthreads=NTHREADS)
+    H.assert_close(out[rows], ref, bf16=True)
+    H.assert_lse_close(lse[rows], ref_lse, bf16=True)
+
+
+def test_mixed_varlen_decode_rows_via_split(orc):
+    """The 12 single-token sequences of the mixed batch through split + merge agree with
+    the oracle and with the prefill call's rows."""
+    wl = W.mixed_varlen()
+    dev = H.Device(wl)
+    first = 4
+    q_rows = wl.cu_q[first:-1]
+    q = dev.q[torch.from_numpy(q_rows.astype(np.int64)).cuda()].contiguous()
+    cu_k = dev.cu_k[first:].contiguous()
+    max_lk = int(wl.seqlens_k[first:].max())
+    out, lse = H.run_decode(dev, 2048, q=q, cu_k=cu_k, max_lk=max_lk)
+    ref, ref_lse = orc.workload(wl, rows=q_rows.astype(np.int64), nthreads=NTHREADS)
+    H.assert_close(out, ref, bf16=True)
+    H.assert_lse_close(lse, ref_lse, bf16=True)
+    pout, _ = H.run_prefill(dev)
+    assert np.abs(pout[q_rows] - out).max() <= 2 * H.BF16_MAX_ABS
+
+
+# ---------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("chunk", [4096, 2048, 512, 64, 37, 1])
+def test_split_invariance(orc, chunk):
+    wl = W.random_case(21, batch=3, hq=16, hkv=2, max_k=3000, decode=True,
+                       sink_values=[-np.inf, -20, 0, 20] * 4)
+    dev = H.Device(wl)
+    out, lse = H.run_decode(dev, chunk)
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    H.assert_close(out, ref, bf16=True)
+    H.assert_lse_close(lse, ref_lse, bf16=True)
+
+
+@pytest.mark.parametrize("group", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_group_sizes_prefill(orc, group, dtype):
+    wl = W.random_case(30 + group, dtype=dtype, batch=3, hq=2 * group, hkv=2, max_q=150,
+                       max_k=400)
+    dev = H.Device(wl)
+    out, lse = H.run_prefill(dev)
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    H.assert_close(out, ref, bf16=dtype == "bf16")
+    H.assert_lse_close(lse, ref_lse, bf16=dtype == "bf16")
+
+
+@pytest.mark.parametrize("group", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_group_sizes_decode(orc, group, dtype):
+    wl = W.random_case(50 + group, dtype=dtype, batch=4, hq=2 * group, hkv=2, max_k=700,
+                       decode=True)
+    dev = H.Device(wl)
+    out, lse = H.run_decode(dev, 128)
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    H.assert_close(out, ref, bf16=dtype == "bf16")
+    H.assert_lse_close(lse, ref_lse, bf16=dtype == "bf16")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_ragged_prefill_over_cache(orc, causal):
+    """L_q < L_k with ragged tails, both maskings."""
+    wl = W.make_workload("ragged", dtype="bf16", kind="prefill", seqlens_q=[1, 31, 33, 100, 65],
+                         seqlens_k=[1, 200, 33, 357, 64 + 65], num_q_heads=16, num_kv_heads=2,
+                         head_dim=64, seed=61, causal=causal)
+    dev = H.Device(wl)
+    out, lse = H.run_prefill(dev)
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    H.assert_close(out, ref, bf16=True)
+    H.assert_lse_close(lse, ref_lse, bf16=True)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_empty_and_single_key_sequences(orc, dtype):
+    """Decode with L = 0 (chunk 0 holds only the sink), L = 1, and a sink of -inf with no keys."""
+    wl = W.make_workload("empties", dtype=dtype, kind="decode", seqlens_q=[1, 1, 1, 1],
+                         seqlens_k=[0, 1, 0, 5], num_q_heads=8, num_kv_heads=2, head_dim=64,
+                         seed=62, causal=False,
+                         sink_values=[-np.inf, 0.5, -np.inf, 3.0, -1.0, -np.inf, 20.0, -20.0])
+    dev = H.Device(wl)
+    out, lse = H.run_decode(dev, 4)
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    H.assert_close(out, ref, bf16=dtype == "bf16")
+    H.assert_lse_close(lse, ref_lse, bf16=dtype == "bf16")
+    # the same through the prefill entry point (non-causal, one query per sequence)
+    out2, lse2 = H.run_prefill(dev)
+    H.assert_close(out2, ref, bf16=dtype == "bf16")
+    H.assert_lse_close(lse2, ref_lse, bf16=dtype == "bf16")
+
+
+def test_log2_domain_sinks(orc):
+    """Large sinks next to large scores: a kernel that seeded the base-2 running max with the
+    natural-log sink (or scaled the sink by sm_scale) would be far off here."""
+    rng = np.random.default_rng(63)
+    wl = W.make_workload("log2trap", dtype="bf16", kind="prefill", seqlens_q=[40, 1],
+                         seqlens_k=[40, 300], num_q_heads=8, num_kv_heads=1, head_dim=64, seed=63,
+                         causal=True, sink_values=[20.0, -20.0, 12.0, 5.0, 0.0, -5.0, 8.0, 15.0],
+                         rng=rng)
+    # scale q up so the scores reach the sinks' range
+    wl.q16 = W.bf16_round(wl.q32 * 4.0)
+    wl.q32 = W.bf16_widen(wl.q16)
+    dev = H.Device(wl)
+    out, lse = H.run_prefill(dev)
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    H.assert_close(out, ref, bf16=True)
+    H.assert_lse_close(lse, ref_lse, bf16=True)
+    dout, dlse = H.run_decode(dev, 64, q=dev.q[torch.tensor([39, 40]).cuda()].contiguous())
+    dref, dref_lse = orc.workload(wl, rows=np.array([39, 40]), nthreads=NTHREADS)
+    H.assert_close(dout, dref, bf16=True)
+    H.assert_lse_close(dlse, dref_lse, bf16=True)
+
+
+def test_prefill_rows_equal_decode(orc):
+    """Row i of a causal prefill equals a decode of that query over its visible keys."""
+    wl = W.make_workload("pd", dtype="bf16", kind="prefill", seqlens_q=[70], seqlens_k=[250],
+                         num_q_heads=8, num_kv_heads=1, head_dim=64, seed=64, causal=True)
+    dev = H.Device(wl)
+    out, _ = H.run_prefill(dev)
+    for i in (0, 33, 69):
+        n = 250 - 70 + i + 1
+        cu = torch.tensor([0, n], dtype=torch.int32, device="cuda")
+        dout, _ = H.run_decode(dev, 64, q=dev.q[i:i + 1].contiguous(), cu_k=cu, max_lk=n)
+        assert np.abs(dout[0] - out[i]).max() <= 2 * H.BF16_MAX_ABS

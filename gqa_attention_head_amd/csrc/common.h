@@ -71,6 +71,11 @@ __device__ __forceinline__ bf16x8 concat(bf16x4 lo, bf16x4 hi) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// 16-byte load of data read exactly once (nontemporal: streamed past the caches).
+__device__ __forceinline__ u32x4 load_stream(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }

@@ -4,26 +4,29 @@
 // attention is parallelised across independent heads and along the KV
 // sequence; the online softmax keeps a running maximum m and a running scale
 // d; m starts at the head's sink in the first block of keys only.  This kernel
-// computes, for one (sequence b, KV head g, chunk c), the state (m, d, acc) of
-// all G query heads that share KV head g after the chunk's keys.
+// writes, for every (sequence b, chunk c, query head h), the state (m, d, acc)
+// after chunk c's keys.
 //
-// Work decomposition.  One workgroup of 4 waves per (b, g, c).  The chunk's
-// keys are cut into 32-key tiles dealt round-robin to the waves, so the four
-// waves stream neighbouring K/V rows at the same time.  Each wave keeps its
-// own online-softmax state; the four states are combined through LDS at the
-// end (the same log-sum-exp rule the merge pass uses).
+// Work decomposition (HBM-bound: every K/V byte is read exactly once).
+// One workgroup per (b, c, block of up to 8 KV heads); wave w of the
+// workgroup owns KV head g = 8*block + w and the G query heads that share it.
+// K/V are token-major ([token][kv head][64]), so the 8 waves together stream
+// whole contiguous 1 KB token rows: workgroups never read a fraction of a
+// DRAM row that another workgroup reads later.  With kKSplit = 2 each head is
+// shared by two waves that take alternate 32-key tiles, and the two partial
+// states are combined through LDS at the end.  Each wave keeps kDepth tiles
+// of loads in flight in registers.
 //
 // Per 32-key tile and wave:
-//   S^T[32 keys x 16 heads] = K[32 x 64] . Q^T[64 x 16]      2+2 MFMA 16x16x32
-//     (A = K rows straight from global memory in operand layout, B = the G <= 16
-//      query heads, zero-padded to 16 columns; lane (q4, c16) ends up holding
-//      4+4 scores of head c16)
+//   S^T[32 keys x 16 heads] = K[32 x 64] . Q^T[64 x 16]      4 MFMA 16x16x32
+//     (A = K rows loaded from global memory directly in operand layout,
+//      B = the G <= 16 query heads zero-padded to 16 columns; lane (q4, c16)
+//      then holds 4+4 scores of head c16)
 //   online-softmax update in base 2 (scores pre-multiplied by sm_scale*log2 e)
 //   O^T[64 dims x 16 heads] += V^T[64 x 32] . P^T[32 x 16]  4 MFMA 16x16x32
 //     (V staged row-major in this wave's LDS slice and read back transposed
 //      with ds_read_b64_tr_b16; P^T is the exponentiated S^T tile converted to
-//      bf16 in place, no data movement)
-// K is half of the bytes and V the other half; both are read exactly once.
+//      bf16 in place)
 #include "common.h"
 #include "kernels.h"
 
@@ -32,13 +35,12 @@ namespace sa {
 namespace {
 
 constexpr int kD = 64;
-constexpr int kWaves = 4;
 constexpr int kTile = 32;            // keys per wave iteration
 constexpr int kVStride = kD + 8;     // LDS row stride in bf16 elements (144 bytes)
 
 struct DecodeTile {
     bf16x8 ka[2][2];   // K operand: [key block][dim half]
-    u32x4 vr[4];       // 4 rows' worth of 16-byte V segments
+    u32x4 vr[4];       // four 16-byte V segments (rows lane/8 + 8r)
 };
 
 __device__ __forceinline__ void load_tile(DecodeTile& t, const uint16_t* __restrict__ kbase,
@@ -49,31 +51,92 @@ __device__ __forceinline__ void load_tile(DecodeTile& t, const uint16_t* __restr
     for (int kb = 0; kb < 2; ++kb) {
         const int key = min(t0 + 16 * kb + c16, hi - 1);
         const uint16_t* kp = kbase + (int64_t)key * row_stride + 8 * q4;
-        t.ka[kb][0] = load_bf16x8(kp);
-        t.ka[kb][1] = load_bf16x8(kp + 32);
+        t.ka[kb][0] = __builtin_bit_cast(bf16x8, load_stream(kp));
+        t.ka[kb][1] = __builtin_bit_cast(bf16x8, load_stream(kp + 32));
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int key = min(t0 + lane / 8 + 8 * r, hi - 1);
-        t.vr[r] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * row_stride + 8 * (lane % 8));
+        t.vr[r] = load_stream(vbase + (int64_t)key * row_stride + 8 * (lane % 8));
+    }
+    // Keep the loads where they are issued: the scheduler would otherwise move
+    // them next to their first use and the prefetch would be lost.
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+struct WaveState {
+    float m;       // running max, base 2 (uniform over the 4 lane groups of a head column)
+    float dl;      // this lane's share of the running scale
+    f32x4 o[4];    // O^T[dim 16*mt + 4*q4 + i][head c16]
+};
+
+__device__ __forceinline__ void process_tile(WaveState& st, const DecodeTile& cur, bf16x8 qb0,
+                                             bf16x8 qb1, uint16_t* vw, int t0, int hi,
+                                             float scale_log2, int lane) {
+    const int q4 = lane / 16, c16 = lane % 16;
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    s0 = mfma16x16x32(cur.ka[0][0], qb0, s0);
+    s0 = mfma16x16x32(cur.ka[0][1], qb1, s0);
+    s1 = mfma16x16x32(cur.ka[1][0], qb0, s1);
+    s1 = mfma16x16x32(cur.ka[1][1], qb1, s1);
+
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<u32x4*>(vw + (lane / 8 + 8 * r) * kVStride + 8 * (lane % 8)) = cur.vr[r];
+
+    // s0[i]: key t0 + 4*q4 + i; s1[i]: key t0 + 16 + 4*q4 + i; column = head c16.
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[i] = (t0 + 4 * q4 + i < hi) ? s0[i] * scale_log2 : kNegInf;
+        x[4 + i] = (t0 + 16 + 4 * q4 + i < hi) ? s1[i] * scale_log2 : kNegInf;
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                       fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    tmax = fmaxf(tmax, xor16(tmax));
+    tmax = max_xor32(tmax);
+    const float m_new = fmaxf(st.m, tmax);
+    const bool live = m_new != kNegInf;
+    const float alpha = live ? fast_exp2(st.m - m_new) : 1.0f;
+    const float msub = live ? m_new : 0.0f;
+    float psum = 0.0f;
+    bf16x8 pb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float p = fast_exp2(x[i] - msub);
+        psum += p;
+        pb[i] = static_cast<__bf16>(p);
+    }
+    st.dl = st.dl * alpha + psum;
+    st.m = m_new;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) st.o[mt] *= alpha;
+
+    wave_lds_sync();
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const uint16_t* p0 = vw + (4 * q4 + c16 / 4) * kVStride + 16 * mt + 4 * (c16 % 4);
+        const bf16x8 va = concat(lds_read_tr16(p0), lds_read_tr16(p0 + 16 * kVStride));
+        st.o[mt] = mfma16x16x32(va, pb, st.o[mt]);
     }
 }
 
-template <int G>
-__global__ __launch_bounds__(256) void decode_split_mfma(
+template <int G, int kDepth, int kKSplit, int kHeadsPerBlock>
+__global__ __launch_bounds__(64 * kHeadsPerBlock * kKSplit) void decode_split_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ sinks,
     const int32_t* __restrict__ cu_k, int hq, int hkv, int chunk, int max_chunks,
-    float scale_log2, float* __restrict__ part_m, float* __restrict__ part_d,
-    float* __restrict__ part_acc) {
+    int head_blocks, float scale_log2, float* __restrict__ part_m,
+    float* __restrict__ part_d, float* __restrict__ part_acc) {
+    constexpr int kWaves = kHeadsPerBlock * kKSplit;
     __shared__ uint16_t vlds[kWaves][kTile * kVStride];
-    __shared__ float wm[kWaves][G];
-    __shared__ float wd[kWaves][G];
-    __shared__ float wacc[kWaves][G][kD];
+    constexpr int kX = kKSplit > 1 ? kKSplit - 1 : 1;   // states handed to part 0
+    __shared__ float xm[kX][kHeadsPerBlock][G];
+    __shared__ float xd[kX][kHeadsPerBlock][G];
+    __shared__ float xacc[kX][kHeadsPerBlock][G][kD];
 
-    // KV head fastest so the workgroups of one (b, c) read whole 1 KB token rows together.
-    const int g = blockIdx.x % hkv;
-    const int t = blockIdx.x / hkv;
+    const int hb = blockIdx.x % head_blocks;
+    const int t = blockIdx.x / head_blocks;
     const int c = t % max_chunks;
     const int b = t / max_chunks;
     const int k0 = cu_k[b];
@@ -84,13 +147,30 @@ __global__ __launch_bounds__(256) void decode_split_mfma(
     const int hi = min(lo + chunk, len);
 
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int hw = wave % kHeadsPerBlock;   // head slot in the workgroup
+    const int part = wave / kHeadsPerBlock; // which alternate tiles this wave takes
+    const int g = hb * kHeadsPerBlock + hw;
+    const bool g_ok = g < hkv;
     const int q4 = lane / 16, c16 = lane % 16;
-    const bool head_ok = c16 < G;
+    const bool head_ok = g_ok && c16 < G;
     const int h = g * G + c16;
     const int row_stride = hkv * kD;
-    const uint16_t* kbase = k + ((int64_t)k0 * hkv + g) * kD;
-    const uint16_t* vbase = v + ((int64_t)k0 * hkv + g) * kD;
+    const int gsafe = g_ok ? g : 0;
+    const uint16_t* kbase = k + ((int64_t)k0 * hkv + gsafe) * kD;
+    const uint16_t* vbase = v + ((int64_t)k0 * hkv + gsafe) * kD;
 
+    // m starts at the sink in chunk 0 only; the scale starts at 1, held by one
+    // lane share (q4 == 0) of the first wave of the head.
+    WaveState st;
+    st.m = (c == 0 && head_ok && part == 0) ? sinks[h] * kLog2e : kNegInf;
+    st.dl = (q4 == 0 && part == 0) ? 1.0f : 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) st.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    uint16_t* vw = vlds[wave];
+    constexpr int kStep = kTile * kKSplit;          // distance between this wave's tiles
+    const int first = lo + kTile * part;
+    const int ntiles = (g_ok && first < hi) ? ceil_div(hi - first, kStep) : 0;
     // B operand of S^T = K Q^T: lane holds Q[head c16][dims 8*q4 .. +7] (and +32).
     bf16x8 qb0 = {}, qb1 = {};
     if (head_ok) {
@@ -99,109 +179,79 @@ __global__ __launch_bounds__(256) void decode_split_mfma(
         qb1 = load_bf16x8(qp + 32);
     }
 
-    // Running state in base-2 units.  m starts at the sink in chunk 0 only; the
-    // scale d (whose initial 1 is the sink's own term) is spread over lanes and
-    // waves as partial sums, so exactly one lane per head carries that 1.
-    float m = (c == 0 && head_ok) ? sinks[h] * kLog2e : kNegInf;
-    float dl = (wave == 0 && q4 == 0) ? 1.0f : 0.0f;
-    f32x4 o[4];
+    // kDepth tiles of loads stay in flight per wave.  Loads are issued
+    // unconditionally (addresses clamped to the chunk's last key, which exists
+    // when ntiles > 0), so every tile has exactly the same number of loads
+    // issued after it and the wait before a tile covers that tile's loads only;
+    // the loop body is branch-free (a tile past the chunk's end has every key
+    // masked and leaves the state unchanged).
+    if (ntiles > 0) {
+        DecodeTile buf[kDepth];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    uint16_t* vw = vlds[wave];
-    const int stride = kTile * kWaves;
-    int t0 = lo + kTile * wave;
-    DecodeTile cur;
-    if (t0 < hi) load_tile(cur, kbase, vbase, row_stride, t0, hi, lane);
-    for (; t0 < hi; t0 += stride) {
-        DecodeTile nxt;
-        const bool more = t0 + stride < hi;
-        if (more) load_tile(nxt, kbase, vbase, row_stride, t0 + stride, hi, lane);
-
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-        s0 = mfma16x16x32(cur.ka[0][0], qb0, s0);
-        s0 = mfma16x16x32(cur.ka[0][1], qb1, s0);
-        s1 = mfma16x16x32(cur.ka[1][0], qb0, s1);
-        s1 = mfma16x16x32(cur.ka[1][1], qb1, s1);
-
+        for (int d = 0; d < kDepth; ++d)
+            load_tile(buf[d], kbase, vbase, row_stride, first + d * kStep, hi, lane);
+        int it = 0;
+        do {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            *reinterpret_cast<u32x4*>(vw + (lane / 8 + 8 * r) * kVStride + 8 * (lane % 8)) = cur.vr[r];
-
-        // s0[i]: key t0 + 4*q4 + i; s1[i]: key t0 + 16 + 4*q4 + i; column = head c16.
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[i] = (t0 + 4 * q4 + i < hi) ? s0[i] * scale_log2 : kNegInf;
-            x[4 + i] = (t0 + 16 + 4 * q4 + i < hi) ? s1[i] * scale_log2 : kNegInf;
-        }
-        float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                           fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-        tmax = fmaxf(tmax, xor16(tmax));
-        tmax = max_xor32(tmax);
-        const float m_new = fmaxf(m, tmax);
-        const bool live = m_new != kNegInf;
-        const float alpha = live ? fast_exp2(m - m_new) : 1.0f;
-        const float msub = live ? m_new : 0.0f;
-        float psum = 0.0f;
-        bf16x8 pb;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float p = fast_exp2(x[i] - msub);
-            psum += p;
-            pb[i] = static_cast<__bf16>(p);
-        }
-        dl = dl * alpha + psum;
-        m = m_new;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) o[mt] *= alpha;
-
-        wave_lds_sync();
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const uint16_t* p0 = vw + (4 * q4 + c16 / 4) * kVStride + 16 * mt + 4 * (c16 % 4);
-            const bf16x8 va = concat(lds_read_tr16(p0), lds_read_tr16(p0 + 16 * kVStride));
-            o[mt] = mfma16x16x32(va, pb, o[mt]);
-        }
-        if (more) cur = nxt;
+            for (int d = 0; d < kDepth; ++d) {
+                const int ts = first + (it + d) * kStep;
+                process_tile(st, buf[d], qb0, qb1, vw, ts, hi, scale_log2, lane);
+                load_tile(buf[d], kbase, vbase, row_stride, ts + kDepth * kStep, hi, lane);
+            }
+            it += kDepth;
+        } while (it < ntiles);
     }
 
     // Reduce the scale over the four lane groups of each head column.
-    dl += xor16(dl);
-    dl = sum_xor32(dl);
-    if (head_ok) {
-        if (q4 == 0) {
-            wm[wave][c16] = m;
-            wd[wave][c16] = dl;
-        }
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) wacc[wave][c16][16 * mt + 4 * q4 + i] = o[mt][i];
-    }
-    __syncthreads();
+    st.dl += xor16(st.dl);
+    st.dl = sum_xor32(st.dl);
 
-    for (int idx = threadIdx.x; idx < G * kD; idx += 64 * kWaves) {
-        const int hh = idx / kD, dim = idx % kD;
-        float big = kNegInf;
+    if (kKSplit > 1) {
+        // Parts 1.. hand their states to part 0, which combines them (log-sum-exp).
+        if (part > 0 && head_ok) {
+            if (q4 == 0) {
+                xm[part - 1][hw][c16] = st.m;
+                xd[part - 1][hw][c16] = st.dl;
+            }
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) big = fmaxf(big, wm[w][hh]);
-        const int64_t slot = ((int64_t)b * hq + g * G + hh) * max_chunks + c;
-        float dsum = 1.0f, acc = 0.0f;
-        if (big != kNegInf) {
-            dsum = 0.0f;
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const float wt = fast_exp2(wm[w][hh] - big);
-                dsum += wt * wd[w][hh];
-                acc += wt * wacc[w][hh][dim];
+                for (int i = 0; i < 4; ++i)
+                    xacc[part - 1][hw][c16][16 * mt + 4 * q4 + i] = st.o[mt][i];
+        }
+        __syncthreads();
+        if (part != 0) return;
+        if (head_ok) {
+            float big = st.m;
+#pragma unroll
+            for (int p = 0; p < kKSplit - 1; ++p) big = fmaxf(big, xm[p][hw][c16]);
+            if (big != kNegInf) {
+                const float w0 = fast_exp2(st.m - big);
+                st.dl *= w0;
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) st.o[mt] *= w0;
+#pragma unroll
+                for (int p = 0; p < kKSplit - 1; ++p) {
+                    const float w = fast_exp2(xm[p][hw][c16] - big);
+                    st.dl += w * xd[p][hw][c16];
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            st.o[mt][i] += w * xacc[p][hw][c16][16 * mt + 4 * q4 + i];
+                }
+                st.m = big;
             }
         }
-        part_acc[slot * kD + dim] = acc;
-        if (dim == 0) {
-            part_m[slot] = (big == kNegInf) ? kNegInf : big * kLn2;
-            part_d[slot] = dsum;
-        }
+    }
+    if (!head_ok) return;
+    const int64_t slot = ((int64_t)b * hq + h) * max_chunks + c;
+    float* pa = part_acc + slot * kD;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) *reinterpret_cast<f32x4*>(pa + 16 * mt + 4 * q4) = st.o[mt];
+    if (q4 == 0) {
+        part_m[slot] = (st.m == kNegInf) ? kNegInf : st.m * kLn2;
+        part_d[slot] = st.dl;
     }
 }
 
@@ -210,11 +260,13 @@ hipError_t launch_g(const void* q, const void* k, const void* v, const float* si
                     const int32_t* cu_k, int batch, int hq, int hkv, int chunk, int max_chunks,
                     float sm_scale, float* part_m, float* part_d, float* part_acc,
                     hipStream_t stream) {
-    const int64_t blocks = (int64_t)batch * max_chunks * hkv;
-    hipLaunchKernelGGL((decode_split_mfma<G>), dim3((unsigned)blocks), dim3(64 * kWaves), 0,
-                       stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, sinks,
-                       cu_k, hq, hkv, chunk, max_chunks, sm_scale * kLog2e, part_m, part_d,
-                       part_acc);
+    constexpr int kDepth = 2, kKSplit = 1, kHeadsPerBlock = 8;
+    const int head_blocks = ceil_div(hkv, kHeadsPerBlock);
+    const int64_t blocks = (int64_t)batch * max_chunks * head_blocks;
+    hipLaunchKernelGGL((decode_split_mfma<G, kDepth, kKSplit, kHeadsPerBlock>), dim3((unsigned)blocks),
+                       dim3(64 * kHeadsPerBlock * kKSplit), 0, stream, (const uint16_t*)q,
+                       (const uint16_t*)k, (const uint16_t*)v, sinks, cu_k, hq, hkv, chunk,
+                       max_chunks, head_blocks, sm_scale * kLog2e, part_m, part_d, part_acc);
     return hipGetLastError();
 }
 

@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of grouped-query attention with per-head sinks on one MI355X.
 
-One step = split-KV decode (split pass + log-sum-exp merge) of the batched
+One step = one split-KV decode call (split pass + log-sum-exp merge, issued as a
+single fused launch) of the batched
 gpt-oss-shaped decode workload: 32 sequences x 1 query token over 4096 cached
 keys, 64 query heads on 8 KV heads, head_dim 64, bf16, 8 KV chunks per
 sequence.  `value` is the K/V bytes that step reads (268,435,456 B) divided by
@@ -63,35 +64,27 @@ def bench_decode(steps: int, warmup: int):
     max_lk = int(wl.seqlens_k.max())
     chunk = wl.kv_chunk
     nch = -(-max_lk // chunk)
-    parts = sa.partial_buffers(wl.batch, wl.num_q_heads, nch, wl.head_dim, dev)
+    ws = sa.DecodeWorkspace(wl.batch, wl.num_q_heads, wl.num_kv_heads, nch, wl.head_dim, dev)
     out = torch.empty(wl.batch, wl.num_q_heads, wl.head_dim, device=dev, dtype=torch.bfloat16)
     lse = torch.empty(wl.batch, wl.num_q_heads, device=dev, dtype=torch.float32)
 
-    def step(i, ev=None):
+    def step(i):
         j = i % KV_COPIES
-        if ev is not None:
-            ev[0].record()
-        sa.decode_split(q, ks[j], vs[j], sinks, cu_k, max_lk, chunk, nch, wl.sm_scale,
-                        partials=parts)
-        if ev is not None:
-            ev[1].record()
-        sa.merge(*parts, cu_k, chunk, out=out, lse=lse)
-        if ev is not None:
-            ev[2].record()
+        sa.decode(q, ks[j], vs[j], sinks, cu_k, max_lk, chunk, wl.sm_scale, workspace=ws,
+                  out=out, lse=lse)
 
     for i in range(warmup):
         step(i)
     _sync()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    t0 = time.perf_counter()
+    # per-launch durations with events on the stream the kernel runs on
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for i in range(steps):
-        step(i, evs[i])
+        evs[i][0].record()
+        step(i)
+        evs[i][1].record()
     _sync()
-    wall = time.perf_counter() - t0
-    split_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    merge_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
-    # untimed-by-events pass for the step time (no events between the launches)
+    launch_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    # the timed steps: nothing between the launches
     _sync()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -103,10 +96,8 @@ def bench_decode(steps: int, warmup: int):
     return dict(
         workload=wl.name, kv_bytes=kv_bytes, ms_per_step=ms_per_step,
         gbs=kv_bytes / (ms_per_step * 1e-3) / 1e9,
-        split_ms_mean=float(split_ms.mean()), split_ms_median=float(np.median(split_ms)),
-        merge_ms_mean=float(merge_ms.mean()), event_step_ms_mean=float(step_ms.mean()),
-        wall_ms_with_events=wall * 1e3 / steps, batch=wl.batch, kv_len=int(max_lk), chunk=chunk,
-        num_chunks=nch, wl=wl)
+        launch_ms_mean=float(launch_ms.mean()), launch_ms_median=float(np.median(launch_ms)),
+        batch=wl.batch, kv_len=int(max_lk), chunk=chunk, num_chunks=nch, wl=wl)
 
 
 def bench_prefill(steps: int, warmup: int):
@@ -213,7 +204,7 @@ def main(argv=None):
         cpu = cpu_baseline(dec["wl"], pre["wl"] if pre else __import__(
             "gqa_attention_head_amd.workloads", fromlist=["x"]).causal_prefill())
 
-    split_gbs = dec["kv_bytes"] / (dec["split_ms_mean"] * 1e-3) / 1e9
+    kernel_gbs = dec["kv_bytes"] / (dec["launch_ms_mean"] * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": round(dec["gbs"], 2),
@@ -232,11 +223,10 @@ def main(argv=None):
                    "kv_chunk": dec["chunk"], "num_chunks": dec["num_chunks"],
                    "kv_copies_rotated": KV_COPIES, "parallelism": "single-gpu"},
         "hbm_frac": round(dec["gbs"] / HBM_PEAK_GBS, 4),
-        "decode_kernels_ms": {"split_mean": round(dec["split_ms_mean"], 5),
-                              "merge_mean": round(dec["merge_ms_mean"], 5)},
-        "roofline": {"kernel": "decode_split_mfma<8>", "bound": "hbm",
-                     "achieved": round(split_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(split_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "roofline": {"kernel": "decode_split_mfma<8, fused merge>", "bound": "hbm",
+                     "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(kernel_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "launch_ms_mean": round(dec["launch_ms_mean"], 5)},
     }
     if pre is not None:
         line["prefill"] = {

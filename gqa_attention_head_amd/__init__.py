@@ -21,7 +21,7 @@ LIBRARY = os.path.join(PKG, "libsinkattn.so")
 SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_ELAUNCH = 0, 1, 2, 3
 SA_FP32, SA_BF16 = 0, 1
 EXPORTS = ("sink_attn_prefill", "sink_attn_decode_split", "sink_attn_merge",
-           "sink_attn_last_error")
+           "sink_attn_decode", "sink_attn_last_error")
 
 
 class SinkAttnError(RuntimeError):
@@ -57,6 +57,9 @@ def load_library():
     lib.sink_attn_merge.restype = ctypes.c_int
     lib.sink_attn_merge.argtypes = [ctypes.c_int, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp,
                                     vp, vp]
+    lib.sink_attn_decode.restype = ctypes.c_int
+    lib.sink_attn_decode.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                     i32, i32, f32, vp, vp, vp, vp, vp, vp, vp]
     lib.sink_attn_last_error.restype = ctypes.c_char_p
     lib.sink_attn_last_error.argtypes = []
     _lib = lib
@@ -191,12 +194,49 @@ def merge(part_m, part_d, part_acc, cu_seqlens_k, kv_chunk_size, out_dtype=None,
     return (out, lse) if return_lse else out
 
 
+class DecodeWorkspace:
+    """Caller-owned scratch of ``decode``: chunk states and per-sequence arrival counters
+    (zeroed once here; every call leaves them zero)."""
+
+    def __init__(self, batch, num_q_heads, num_kv_heads, max_num_chunks, head_dim=64,
+                 device="cuda"):
+        torch = _torch()
+        self.max_num_chunks = int(max_num_chunks)
+        self.partials = partial_buffers(batch, num_q_heads, self.max_num_chunks, head_dim, device)
+        self.counters = torch.zeros(batch * num_kv_heads, dtype=torch.int32, device=device)
+
+
 def decode(q, k, v, sinks, cu_seqlens_k, max_seqlen_k, kv_chunk_size, sm_scale,
-           max_num_chunks=None, partials=None, out=None, lse=None, return_lse=False, stream=None):
-    """Split-KV decode: ``decode_split`` then ``merge`` on the same stream."""
+           max_num_chunks=None, workspace=None, out=None, lse=None, return_lse=False,
+           stream=None):
+    """Split-KV decode in one call (``sink_attn_decode``): split pass and merge, fused into a
+    single launch where the library supports it."""
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name, q.dtype)
+    _dev(sinks, "sinks", torch.float32)
+    _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32)
+    batch = cu_seqlens_k.numel() - 1
+    if q.dim() != 3 or q.shape[0] != batch:
+        raise ValueError("q must be [batch, Hq, D] with batch = len(cu_seqlens_k) - 1")
     if max_num_chunks is None:
-        max_num_chunks = max(1, -(-int(max_seqlen_k) // int(kv_chunk_size)))
-    pm, pd, pa = decode_split(q, k, v, sinks, cu_seqlens_k, max_seqlen_k, kv_chunk_size,
-                              max_num_chunks, sm_scale, partials=partials, stream=stream)
-    return merge(pm, pd, pa, cu_seqlens_k, kv_chunk_size, out_dtype=q.dtype, out=out, lse=lse,
-                 return_lse=return_lse, stream=stream)
+        max_num_chunks = (workspace.max_num_chunks if workspace is not None
+                          else max(1, -(-int(max_seqlen_k) // int(kv_chunk_size))))
+    if workspace is None:
+        workspace = DecodeWorkspace(batch, q.shape[1], k.shape[1], max_num_chunks, q.shape[2],
+                                    q.device)
+    pm, pd, pa = workspace.partials
+    _dev(workspace.counters, "counters", torch.int32)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    if lse is None and return_lse:
+        lse = torch.empty(batch, q.shape[1], device=q.device, dtype=torch.float32)
+    _dev(lse, "lse", torch.float32)
+    _check(lib.sink_attn_decode(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(sinks),
+                                _ptr(cu_seqlens_k), batch, q.shape[1], k.shape[1], q.shape[2],
+                                int(max_seqlen_k), int(kv_chunk_size), int(max_num_chunks),
+                                float(sm_scale), _ptr(pm), _ptr(pd), _ptr(pa),
+                                _ptr(workspace.counters), _ptr(out), _ptr(lse), _stream(stream)))
+    return (out, lse) if return_lse else out

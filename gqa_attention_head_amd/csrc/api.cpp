@@ -109,16 +109,20 @@ sa_status_t sink_attn_prefill(sa_dtype_t dtype, const void* q, const void* k, co
     return finish_launch(e, st, "sink_attn_prefill");
 }
 
-sa_status_t sink_attn_decode_split(sa_dtype_t dtype, const void* q, const void* k, const void* v,
-                                   const float* sinks, const int32_t* cu_seqlens_k, int32_t batch,
-                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                   int32_t max_seqlen_k, int32_t kv_chunk_size,
-                                   int32_t max_num_chunks, float sm_scale, float* part_m,
-                                   float* part_d, float* part_acc, void* stream) {
+}  // extern "C"
+
+namespace {
+
+sa_status_t check_split_args(sa_dtype_t dtype, const void* q, const void* k, const void* v,
+                             const float* sinks, const int32_t* cu_seqlens_k, int32_t batch,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t max_seqlen_k, int32_t kv_chunk_size, int32_t max_num_chunks,
+                             float sm_scale, const float* part_m, const float* part_d,
+                             const float* part_acc) {
     sa_status_t s;
     if ((s = check_dtype(dtype)) != SA_OK) return s;
     if (!q || !k || !v || !sinks || !cu_seqlens_k || !part_m || !part_d || !part_acc)
-        return fail(SA_EINVAL, "sink_attn_decode_split: null pointer argument");
+        return fail(SA_EINVAL, "decode: null pointer argument");
     if ((s = check_heads(batch, num_q_heads, num_kv_heads, head_dim)) != SA_OK) return s;
     if (kv_chunk_size < 1) return fail(SA_EINVAL, "kv_chunk_size must be >= 1, got %d", kv_chunk_size);
     if (max_seqlen_k < 0) return fail(SA_EINVAL, "max_seqlen_k must be >= 0");
@@ -127,23 +131,74 @@ sa_status_t sink_attn_decode_split(sa_dtype_t dtype, const void* q, const void* 
         return fail(SA_EINVAL, "max_num_chunks (%d) < ceil(max_seqlen_k / kv_chunk_size) = %lld",
                     max_num_chunks, (long long)need);
     if (!std::isfinite(sm_scale)) return fail(SA_EINVAL, "sm_scale must be finite");
-    const int group = num_q_heads / num_kv_heads;
-    const bool mfma = dtype == SA_BF16 && sa::mfma_decode_supported(group);
-    if (mfma && (int64_t)batch * max_num_chunks * num_kv_heads > 0x7fffffffLL)
+    if ((int64_t)batch * max_num_chunks * num_kv_heads > 0x7fffffffLL)
         return fail(SA_EINVAL, "batch * max_num_chunks * Hkv exceeds the grid limit");
-    if (!mfma && max_num_chunks > 0x7fffffff) return fail(SA_EINVAL, "max_num_chunks too large");
+    return SA_OK;
+}
+
+hipError_t launch_split(sa_dtype_t dtype, const void* q, const void* k, const void* v,
+                        const float* sinks, const int32_t* cu_seqlens_k, int32_t batch,
+                        int32_t hq, int32_t hkv, int32_t chunk, int32_t max_num_chunks,
+                        float sm_scale, float* part_m, float* part_d, float* part_acc,
+                        hipStream_t st) {
+    if (dtype == SA_BF16 && sa::mfma_decode_supported(hq / hkv))
+        return sa::launch_mfma_decode_split(q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, chunk,
+                                            max_num_chunks, sm_scale, part_m, part_d, part_acc, st);
+    return sa::launch_generic_decode_split(dtype == SA_BF16, q, k, v, sinks, cu_seqlens_k, batch,
+                                           hq, hkv, chunk, max_num_chunks, sm_scale, part_m,
+                                           part_d, part_acc, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+sa_status_t sink_attn_decode_split(sa_dtype_t dtype, const void* q, const void* k, const void* v,
+                                   const float* sinks, const int32_t* cu_seqlens_k, int32_t batch,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t max_seqlen_k, int32_t kv_chunk_size,
+                                   int32_t max_num_chunks, float sm_scale, float* part_m,
+                                   float* part_d, float* part_acc, void* stream) {
+    sa_status_t s = check_split_args(dtype, q, k, v, sinks, cu_seqlens_k, batch, num_q_heads,
+                                     num_kv_heads, head_dim, max_seqlen_k, kv_chunk_size,
+                                     max_num_chunks, sm_scale, part_m, part_d, part_acc);
+    if (s != SA_OK) return s;
     if ((s = check_device()) != SA_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e;
-    if (mfma)
-        e = sa::launch_mfma_decode_split(q, k, v, sinks, cu_seqlens_k, batch, num_q_heads,
-                                         num_kv_heads, kv_chunk_size, max_num_chunks, sm_scale,
-                                         part_m, part_d, part_acc, st);
-    else
-        e = sa::launch_generic_decode_split(dtype == SA_BF16, q, k, v, sinks, cu_seqlens_k, batch,
-                                            num_q_heads, num_kv_heads, kv_chunk_size,
-                                            max_num_chunks, sm_scale, part_m, part_d, part_acc, st);
+    hipError_t e = launch_split(dtype, q, k, v, sinks, cu_seqlens_k, batch, num_q_heads,
+                                num_kv_heads, kv_chunk_size, max_num_chunks, sm_scale, part_m,
+                                part_d, part_acc, st);
     return finish_launch(e, st, "sink_attn_decode_split");
+}
+
+sa_status_t sink_attn_decode(sa_dtype_t dtype, const void* q, const void* k, const void* v,
+                             const float* sinks, const int32_t* cu_seqlens_k, int32_t batch,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t max_seqlen_k, int32_t kv_chunk_size, int32_t max_num_chunks,
+                             float sm_scale, float* part_m, float* part_d, float* part_acc,
+                             int32_t* counters, void* out, float* lse, void* stream) {
+    sa_status_t s = check_split_args(dtype, q, k, v, sinks, cu_seqlens_k, batch, num_q_heads,
+                                     num_kv_heads, head_dim, max_seqlen_k, kv_chunk_size,
+                                     max_num_chunks, sm_scale, part_m, part_d, part_acc);
+    if (s != SA_OK) return s;
+    if (!counters || !out) return fail(SA_EINVAL, "sink_attn_decode: null pointer argument");
+    if ((s = check_device()) != SA_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool fused = dtype == SA_BF16 && sa::mfma_decode_supported(num_q_heads / num_kv_heads) &&
+                       max_num_chunks <= sa::kFusedMaxChunks;
+    hipError_t e;
+    if (fused) {
+        e = sa::launch_mfma_decode_fused(q, k, v, sinks, cu_seqlens_k, batch, num_q_heads,
+                                         num_kv_heads, kv_chunk_size, max_num_chunks, sm_scale,
+                                         part_m, part_d, part_acc, counters, out, lse, st);
+    } else {
+        e = launch_split(dtype, q, k, v, sinks, cu_seqlens_k, batch, num_q_heads, num_kv_heads,
+                         kv_chunk_size, max_num_chunks, sm_scale, part_m, part_d, part_acc, st);
+        if (e == hipSuccess)
+            e = sa::launch_merge(dtype == SA_BF16, part_m, part_d, part_acc, cu_seqlens_k,
+                                 kv_chunk_size, max_num_chunks, batch, num_q_heads, out, lse, st);
+    }
+    return finish_launch(e, st, "sink_attn_decode");
 }
 
 sa_status_t sink_attn_merge(sa_dtype_t out_dtype, const float* part_m, const float* part_d,

@@ -76,6 +76,31 @@ __device__ __forceinline__ u32x4 load_stream(const uint16_t* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// Device-scope coherent float store/load (relaxed): visible to workgroups on
+// every XCD without flushing or invalidating the per-XCD L2 caches.
+__device__ __forceinline__ void store_coherent(float* p, float x) {
+    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 16-byte device-coherent loads and stores of a float array through a buffer
+// resource (cache policy SC1, the same bit the device-scope atomics above use).
+struct CoherentBuffer {
+    static constexpr int kSC1 = 16;                  // cache-policy bit of the access
+    static constexpr unsigned kRawDword3 = 0x00020000u;
+    __amdgpu_buffer_rsrc_t rsrc;
+    __device__ CoherentBuffer(float* base, int n_floats)
+        : rsrc(__builtin_amdgcn_make_buffer_rsrc(base, 0, n_floats * 4, kRawDword3)) {}
+    __device__ void store4(int idx, f32x4 x) const {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rsrc, idx * 4, 0, kSC1);
+    }
+    __device__ f32x4 load4(int idx) const {
+        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, idx * 4, 0, kSC1));
+    }
+};
+
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }

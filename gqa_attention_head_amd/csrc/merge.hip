@@ -8,9 +8,9 @@
 // lse = M + ln sum_c w_c d_c.  The sink already sits in chunk 0's state.
 //
 // One wave per (sequence, query head); lane = output dimension (head_dim 64).
-// The wave first finds M (lanes stride over the chunks), then every lane
-// sweeps the chunks for its own dimension; the per-chunk weight is computed
-// once per 64 chunks by the lane that owns the chunk and broadcast from LDS.
+// The wave first finds M (lanes stride over the chunks), then each lane
+// computes the weight of one chunk and the lanes sweep the chunks' rows for
+// their own dimension, the weights broadcast across the wave.
 #include "common.h"
 #include "kernels.h"
 
@@ -27,13 +27,17 @@ __device__ __forceinline__ float wave_max(float x) {
     return x;
 }
 
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
 template <bool kBf16>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void merge_kernel(
     const float* __restrict__ part_m, const float* __restrict__ part_d,
     const float* __restrict__ part_acc, const int32_t* __restrict__ cu_k, int chunk,
     int max_chunks, int batch, int hq, void* __restrict__ out, float* __restrict__ lse) {
-    __shared__ float wts[kWavesPerBlock][64];
-    __shared__ float dws[kWavesPerBlock][64];
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     const int pair = blockIdx.x * kWavesPerBlock + wave;
     if (pair >= batch * hq) return;  // no workgroup barrier below
@@ -49,6 +53,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void merge_kernel(
     float acc = 0.0f, den = 0.0f;
     if (big != kNegInf) {
         for (int c0 = 0; c0 < nch; c0 += 64) {
+            // lane j of the group holds chunk c0 + j's weight
             const int c = c0 + lane;
             float w = 0.0f, dw = 0.0f;
             if (c < nch) {
@@ -56,16 +61,17 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void merge_kernel(
                 w = (mc == kNegInf) ? 0.0f : fast_exp2((mc - big) * kLog2e);
                 dw = w * part_d[base + c];
             }
-            wts[wave][lane] = w;
-            dws[wave][lane] = dw;
-            wave_lds_sync();
+            den += wave_sum(dw);
             const int n = min(64, nch - c0);
-            for (int j = 0; j < n; ++j) {
-                const float wj = wts[wave][j];
-                den += dws[wave][j];
-                if (wj != 0.0f) acc += wj * part_acc[(base + c0 + j) * kD + lane];
+            // lane = output dimension; eight chunk rows in flight at a time
+            for (int j0 = 0; j0 < n; j0 += 8) {
+                float vals[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    vals[u] = (j0 + u < n) ? part_acc[(base + c0 + j0 + u) * kD + lane] : 0.0f;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) acc += __shfl(w, j0 + u) * vals[u];
             }
-            wave_lds_sync();
         }
     }
     const bool empty = (big == kNegInf) || !(den > 0.0f);

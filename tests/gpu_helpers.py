@@ -118,3 +118,21 @@ def assert_lse_close(got, want, bf16: bool):
         err = np.abs(got[fin] - want[fin]).max()
         tol = BF16_LSE if bf16 else FP32_LSE
         assert err <= tol, f"lse: max abs err {err:.3e} > {tol}"
+
+
+def run_decode_fused(dev: Device, chunk: int, q=None, cu_k=None, max_lk=None, workspace=None,
+                     max_num_chunks=None):
+    """One ``sink_attn_decode`` call (fused split + merge where supported)."""
+    wl = dev.wl
+    q = dev.q if q is None else q
+    cu_k = dev.cu_k if cu_k is None else cu_k
+    max_lk = dev.max_lk if max_lk is None else max_lk
+    batch = cu_k.numel() - 1
+    out, obuf = guarded((batch, wl.num_q_heads, wl.head_dim), dev.dtype)
+    lse_t, lbuf = guarded((batch, wl.num_q_heads), torch.float32)
+    sa.decode(q, dev.k, dev.v, dev.sinks, cu_k, max_lk, chunk, wl.sm_scale,
+              max_num_chunks=max_num_chunks, workspace=workspace, out=out, lse=lse_t)
+    torch.cuda.synchronize()
+    check_guard(obuf, out.numel())
+    check_guard(lbuf, lse_t.numel())
+    return out.float().cpu().numpy().astype(np.float64), lse_t.cpu().numpy().astype(np.float64)

@@ -73,6 +73,14 @@ def _split(lib, **kw):
     return lib.sink_attn_decode_split(*a.values())
 
 
+def _decode(lib, **kw):
+    a = dict(dtype=sa.SA_BF16, q=P, k=P, v=P, sinks=P, cu_k=P, batch=2, hq=64, hkv=8, d=64,
+             max_k=4096, chunk=512, max_chunks=8, scale=0.125, pm=P, pd=P, pa=P, counters=P,
+             out=P, lse=NULL, stream=NULL)
+    a.update(kw)
+    return lib.sink_attn_decode(*a.values())
+
+
 def _merge(lib, **kw):
     a = dict(dtype=sa.SA_BF16, pm=P, pd=P, pa=P, cu_k=P, chunk=512, max_chunks=8, batch=2,
              hq=64, d=64, out=P, lse=NULL, stream=NULL)
@@ -114,6 +122,19 @@ def test_decode_split_rejects(lib, kw, status):
 
 
 @pytest.mark.parametrize("kw,status", [
+    (dict(counters=NULL), sa.SA_EINVAL),
+    (dict(out=NULL), sa.SA_EINVAL),
+    (dict(pm=NULL), sa.SA_EINVAL),
+    (dict(max_chunks=7), sa.SA_EINVAL),
+    (dict(hq=64, hkv=5), sa.SA_EINVAL),
+    (dict(d=96), sa.SA_EUNSUPPORTED),
+])
+def test_decode_rejects(lib, kw, status):
+    assert _decode(lib, **kw) == status
+    assert lib.sink_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
     (dict(out=NULL), sa.SA_EINVAL),
     (dict(chunk=0), sa.SA_EINVAL),
     (dict(max_chunks=0), sa.SA_EINVAL),
@@ -135,6 +156,7 @@ def test_valid_call_without_device_reports_launch_error(lib):
     assert "device" in lib.sink_attn_last_error().decode()
     assert _split(lib) == sa.SA_ELAUNCH
     assert _merge(lib) == sa.SA_ELAUNCH
+    assert _decode(lib) == sa.SA_ELAUNCH
 
 
 def test_missing_library_fails_loudly(tmp_path):

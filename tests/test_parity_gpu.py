@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
+import gqa_attention_head_amd as sa
 from gqa_attention_head_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -220,3 +221,57 @@ def test_prefill_rows_equal_decode(orc):
         cu = torch.tensor([0, n], dtype=torch.int32, device="cuda")
         dout, _ = H.run_decode(dev, 64, q=dev.q[i:i + 1].contiguous(), cu_k=cu, max_lk=n)
         assert np.abs(dout[0] - out[i]).max() <= 2 * H.BF16_MAX_ABS
+
+
+# ---------------------------------------------------------------- one-call decode
+
+def test_fused_decode_batched(orc):
+    """The 32 x 4096 decode (8 chunks: single fused launch), twice in a row with one
+    workspace: the arrival counters must come back to zero and the results agree."""
+    wl = W.workload(2)
+    dev = H.Device(wl)
+    ws = sa.DecodeWorkspace(wl.batch, wl.num_q_heads, wl.num_kv_heads, 8)
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    for _ in range(2):
+        out, lse = H.run_decode_fused(dev, wl.kv_chunk, workspace=ws)
+        H.assert_close(out, ref, bf16=True)
+        H.assert_lse_close(lse, ref_lse, bf16=True)
+        assert int(ws.counters.abs().sum().item()) == 0
+
+
+def test_fused_decode_ragged_long(orc):
+    """64 chunk slots per sequence: the call runs split then merge."""
+    wl = W.workload(4)
+    dev = H.Device(wl)
+    out, lse = H.run_decode_fused(dev, wl.kv_chunk)
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    H.assert_close(out, ref, bf16=True)
+    H.assert_lse_close(lse, ref_lse, bf16=True)
+
+
+@pytest.mark.parametrize("group", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("chunk", [37, 256, 4096])
+def test_fused_decode_cases(orc, group, chunk):
+    wl = W.random_case(70 + group, batch=5, hq=2 * group, hkv=2, max_k=1500, decode=True,
+                       sink_values=([-np.inf, 20.0, -20.0, 0.5] * group)[:2 * group])
+    dev = H.Device(wl)
+    ws = sa.DecodeWorkspace(wl.batch, wl.num_q_heads, wl.num_kv_heads,
+                            max(1, -(-dev.max_lk // chunk)))
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    for _ in range(2):
+        out, lse = H.run_decode_fused(dev, chunk, workspace=ws)
+        H.assert_close(out, ref, bf16=True)
+        H.assert_lse_close(lse, ref_lse, bf16=True)
+    assert int(ws.counters.abs().sum().item()) == 0
+
+
+def test_fused_decode_empty_sequences(orc):
+    wl = W.make_workload("empties_fused", dtype="bf16", kind="decode", seqlens_q=[1] * 4,
+                         seqlens_k=[0, 1, 0, 70], num_q_heads=8, num_kv_heads=1, head_dim=64,
+                         seed=77, causal=False,
+                         sink_values=[-np.inf, 0.5, -np.inf, 3.0, -1.0, -np.inf, 20.0, -20.0])
+    dev = H.Device(wl)
+    out, lse = H.run_decode_fused(dev, 32)
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    H.assert_close(out, ref, bf16=True)
+    H.assert_lse_close(lse, ref_lse, bf16=True)

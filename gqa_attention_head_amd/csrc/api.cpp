@@ -93,7 +93,8 @@ sa_status_t sink_attn_prefill(sa_dtype_t dtype, const void* q, const void* k, co
     if (max_seqlen_q < 0 || max_seqlen_k < 0)
         return fail(SA_EINVAL, "max_seqlen_q/max_seqlen_k must be >= 0");
     if (causal != 0 && causal != 1) return fail(SA_EINVAL, "causal must be 0 or 1");
-    if (!std::isfinite(sm_scale)) return fail(SA_EINVAL, "sm_scale must be finite");
+    if (!(std::isfinite(sm_scale) && sm_scale > 0.0f))
+        return fail(SA_EINVAL, "sm_scale must be finite and > 0");
     if (max_seqlen_q == 0) return ok();
     if ((s = check_device()) != SA_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -130,7 +131,8 @@ sa_status_t check_split_args(sa_dtype_t dtype, const void* q, const void* k, con
     if (max_num_chunks < need)
         return fail(SA_EINVAL, "max_num_chunks (%d) < ceil(max_seqlen_k / kv_chunk_size) = %lld",
                     max_num_chunks, (long long)need);
-    if (!std::isfinite(sm_scale)) return fail(SA_EINVAL, "sm_scale must be finite");
+    if (!(std::isfinite(sm_scale) && sm_scale > 0.0f))
+        return fail(SA_EINVAL, "sm_scale must be finite and > 0");
     if ((int64_t)batch * max_num_chunks * num_kv_heads > 0x7fffffffLL)
         return fail(SA_EINVAL, "batch * max_num_chunks * Hkv exceeds the grid limit");
     return SA_OK;

@@ -34,20 +34,40 @@ constexpr int kBK = 64;             // keys per tile
 constexpr int kStride = kD + 8;     // LDS row stride in bf16 elements (144 bytes)
 constexpr int kSegs = kBK * kD / 8; // 16-byte segments per K (or V) tile
 
+// Above this growth of the row maximum (base-2 units) the running state is
+// rescaled; smaller growth keeps the stale maximum, so exponentiated scores stay
+// below 2^kRescaleThreshold and the rescale multiply is skipped for the tile.
+constexpr float kRescaleThreshold = 8.0f;
+
 template <int G>
-__global__ __launch_bounds__(64 * G) void prefill_mfma(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const float* __restrict__ sinks,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int hq, int hkv,
-    int n_qblocks, float scale_log2, int causal, uint16_t* __restrict__ out,
-    float* __restrict__ lse) {
+__global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4)))
+void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                  const uint16_t* __restrict__ v, const float* __restrict__ sinks,
+                  const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int hq,
+                  int hkv, int batch, int n_qblocks, float scale_log2, int causal,
+                  uint16_t* __restrict__ out, float* __restrict__ lse) {
     constexpr int kThreads = 64 * G;
     constexpr int kPer = (kSegs + kThreads - 1) / kThreads;
     __shared__ uint16_t kl[2][kBK * kStride];
     __shared__ uint16_t vl[2][kBK * kStride];
 
-    const int qb = n_qblocks - 1 - (int)blockIdx.x;  // heaviest blocks first
-    const int g = blockIdx.y, b = blockIdx.z;
+    // Work item -> (sequence b, KV head g, query block qb).  Query blocks go
+    // heaviest first (the causal triangle gives late blocks the most keys).
+    // When the (b, g) pairs split evenly over the 8 XCDs (workgroups are dealt
+    // to XCDs round-robin), each XCD keeps its own pairs, so a K/V head is
+    // cached in one XCD's L2 only.
+    const int pairs = batch * hkv;
+    const int bid = blockIdx.x;
+    int pair, qb;
+    if (pairs % 8 == 0) {
+        const int xcd = bid % 8, j = bid / 8, per_xcd = pairs / 8;
+        pair = (j % per_xcd) * 8 + xcd;
+        qb = n_qblocks - 1 - j / per_xcd;
+    } else {
+        pair = bid % pairs;
+        qb = n_qblocks - 1 - bid / pairs;
+    }
+    const int b = pair / hkv, g = pair % hkv;
     const int q0 = cu_q[b], lq = cu_q[b + 1] - q0;
     const int k0 = cu_k[b], lk = cu_k[b + 1] - k0;
     const int r0 = qb * kBQ;
@@ -72,8 +92,10 @@ __global__ __launch_bounds__(64 * G) void prefill_mfma(
         for (int ks = 0; ks < 4; ++ks) qop[ks] = load_bf16x8(qp + 16 * ks);
     }
 
-    float m = sinks[h] * kLog2e;          // running max starts at the sink (base-2 units)
-    float dl = (half == 0) ? 1.0f : 0.0f; // running scale, split over the two lane halves
+    // Running state (base 2): the maximum starts at the sink (the first and only
+    // block of keys holds it) and the scale at 1, split over the two lane halves.
+    float m = sinks[h] * kLog2e;
+    float dl = (half == 0) ? 1.0f : 0.0f;
     f32x16 o[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -123,6 +145,7 @@ __global__ __launch_bounds__(64 * G) void prefill_mfma(
         const uint16_t* kt = kl[buf];
         const uint16_t* vt = vl[buf];
 
+        // raw scores: s[kb][i] = <q_row, k_key>, key = j0 + 32*kb + 8*(i/4) + 4*half + i%4
         f32x16 s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -134,53 +157,60 @@ __global__ __launch_bounds__(64 * G) void prefill_mfma(
                 s[kb] = mfma32x32x16(a, qop[ks], s[kb]);
             }
         }
-        // s[kb][i] = S^T[key j0 + 32*kb + 8*(i/4) + 4*half + i%4][row]
-        const bool need_mask = j0 + kBK > full_end;
+        if (j0 + kBK > full_end) {  // diagonal or ragged tile (uniform)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = j0 + 32 * kb + 8 * (i / 4) + 4 * half + (i % 4);
+                    if (key >= row_lim) s[kb][i] = kNegInf;
+                }
+        }
+        // row max of the tile (sm_scale > 0, so the max of raw scores scales)
         float tmax = kNegInf;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float x = s[kb][i] * scale_log2;
-                if (need_mask) {
-                    const int key = j0 + 32 * kb + 8 * (i / 4) + 4 * half + (i % 4);
-                    if (key >= row_lim) x = kNegInf;
-                }
-                s[kb][i] = x;
-                tmax = fmaxf(tmax, x);
-            }
-        tmax = max_xor32(tmax);
-        const float m_new = fmaxf(m, tmax);
-        const bool live = m_new != kNegInf;
-        const float alpha = live ? fast_exp2(m - m_new) : 1.0f;
-        const float msub = live ? m_new : 0.0f;
-        float psum = 0.0f;
+            for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kb][i]);
+        const float m_cand = max_xor32(tmax) * scale_log2;
+        if (__any(m_cand > m + kRescaleThreshold)) {
+            const float m_new = fmaxf(m, m_cand);
+            const float alpha = (m == kNegInf) ? 0.0f : fast_exp2(m - m_new);
+            dl *= alpha;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = fast_exp2(s[kb][i] - msub);
-                s[kb][i] = p;
-                psum += p;
-            }
-        dl = dl * alpha + psum;
-        m = m_new;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) o[mt] *= alpha;
+            for (int mt = 0; mt < 2; ++mt) o[mt] *= alpha;
+            m = m_new;
+        }
+        const float msub = (m == kNegInf) ? 0.0f : m;
 
+        // P^T tile in bf16, four 16-key slices (the B operand of O^T = V^T P^T);
+        // the running scale accumulates the exponentials in fp32.
+        bf16x8 pb[4];
+        float psum = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int kb = ks / 2, hs = ks % 2;
-            bf16x8 pb;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) pb[i] = static_cast<__bf16>(s[kb][8 * hs + i]);
-            const int key_base = 32 * kb + 16 * hs;
+            for (int e = 0; e < 4; ++e) {
+                const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * hs + 2 * e], scale_log2, -msub));
+                const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * hs + 2 * e + 1], scale_log2, -msub));
+                const bf16x2 pk = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+                pb[ks][2 * e] = pk[0];
+                pb[ks][2 * e + 1] = pk[1];
+                psum += p0 + p1;
+            }
+        }
+        dl += psum;
+
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int key_base = 32 * (ks / 2) + 16 * (ks % 2);
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
                 const uint16_t* p0 = vt + (key_base + 4 * half + c16 / 4) * kStride + 32 * mt +
                                      16 * (g4 % 2) + 4 * (c16 % 4);
                 const bf16x8 va = concat(lds_read_tr16(p0), lds_read_tr16(p0 + 8 * kStride));
-                o[mt] = mfma32x32x16(va, pb, o[mt]);
+                o[mt] = mfma32x32x16(va, pb[ks], o[mt]);
             }
         }
         if (more) lstore(buf ^ 1);
@@ -198,11 +228,12 @@ __global__ __launch_bounds__(64 * G) void prefill_mfma(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             // o[mt][4j + e] = O^T[dim 32*mt + 8*j + 4*half + e][row]
-            uint32_t lo = (uint32_t)f32_to_bf16_bits(o[mt][4 * j + 0] * inv) |
-                          ((uint32_t)f32_to_bf16_bits(o[mt][4 * j + 1] * inv) << 16);
-            uint32_t hi = (uint32_t)f32_to_bf16_bits(o[mt][4 * j + 2] * inv) |
-                          ((uint32_t)f32_to_bf16_bits(o[mt][4 * j + 3] * inv) << 16);
-            *reinterpret_cast<u32x2*>(op + 32 * mt + 8 * j + 4 * half) = u32x2{lo, hi};
+            const bf16x2 lo2 = __builtin_convertvector(
+                f32x2{o[mt][4 * j + 0] * inv, o[mt][4 * j + 1] * inv}, bf16x2);
+            const bf16x2 hi2 = __builtin_convertvector(
+                f32x2{o[mt][4 * j + 2] * inv, o[mt][4 * j + 3] * inv}, bf16x2);
+            *reinterpret_cast<u32x2*>(op + 32 * mt + 8 * j + 4 * half) =
+                u32x2{__builtin_bit_cast(uint32_t, lo2), __builtin_bit_cast(uint32_t, hi2)};
         }
     if (lse != nullptr && half == 0)
         lse[orow] = empty ? kNegInf : (m + fast_log2(dsum)) * kLn2;
@@ -214,10 +245,11 @@ hipError_t launch_g(const void* q, const void* k, const void* v, const float* si
                     int max_lq, float sm_scale, int causal, void* out, float* lse,
                     hipStream_t stream) {
     const int n_qblocks = ceil_div(max_lq, kBQ);
-    dim3 grid(n_qblocks, hkv, batch);
-    hipLaunchKernelGGL((prefill_mfma<G>), grid, dim3(64 * G), 0, stream, (const uint16_t*)q,
-                       (const uint16_t*)k, (const uint16_t*)v, sinks, cu_q, cu_k, hq, hkv,
-                       n_qblocks, sm_scale * kLog2e, causal, (uint16_t*)out, lse);
+    const int64_t blocks = (int64_t)batch * hkv * n_qblocks;
+    hipLaunchKernelGGL((prefill_mfma<G>), dim3((unsigned)blocks), dim3(64 * G), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, sinks, cu_q,
+                       cu_k, hq, hkv, batch, n_qblocks, sm_scale * kLog2e, causal, (uint16_t*)out,
+                       lse);
     return hipGetLastError();
 }
 

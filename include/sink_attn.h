@@ -37,6 +37,7 @@
  *     the HIP runtime rejects the launch or no device is present.  The text
  *     of the last error of the calling thread is returned by
  *     sink_attn_last_error().
+ *   - sm_scale must be finite and > 0 (SA_EINVAL otherwise).
  *   - Device-resident preconditions cannot be checked without a
  *     synchronisation and are the caller's duty: monotone cu_seqlens,
  *     L_q <= L_k for every sequence under causal masking, per-sequence

@@ -101,6 +101,8 @@ def _merge(lib, **kw):
     (dict(causal=2), sa.SA_EINVAL),
     (dict(max_q=-1), sa.SA_EINVAL),
     (dict(scale=float("nan")), sa.SA_EINVAL),
+    (dict(scale=0.0), sa.SA_EINVAL),
+    (dict(scale=-0.125), sa.SA_EINVAL),
 ])
 def test_prefill_rejects(lib, kw, status):
     assert _prefill(lib, **kw) == status

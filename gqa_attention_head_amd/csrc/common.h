@@ -106,6 +106,14 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
+// Direct global->LDS copy of 16 bytes per lane (gfx950): lane l's bytes land at
+// lds_base + 16*l; lds_base must be the same for the whole wave.  The compiler
+// does not track these writes: wait_dma() must precede any read of the data.
+__device__ __forceinline__ void lds_dma16(const uint16_t* src, uint16_t* lds_base) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Orders this wave's earlier LDS writes before its later LDS reads (in-order LDS
 // queue + compiler barrier); used where a wave hands data between its own lanes.
 __device__ __forceinline__ void wave_lds_sync() {

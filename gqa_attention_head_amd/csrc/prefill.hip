@@ -31,7 +31,10 @@ namespace {
 constexpr int kD = 64;
 constexpr int kBQ = 32;             // query rows per wave
 constexpr int kBK = 64;             // keys per tile
-constexpr int kStride = kD + 8;     // LDS row stride in bf16 elements (144 bytes)
+constexpr int kStride = kD + 8;     // LDS row stride of K tiles in bf16 elements (144 bytes)
+// LDS row stride of V tiles (192 bytes): the transposed reads take 64 bytes of
+// four consecutive rows per half-wave, which then fall in distinct banks.
+constexpr int kVStride = kD + 32;
 constexpr int kSegs = kBK * kD / 8; // 16-byte segments per K (or V) tile
 
 // Above this growth of the row maximum (base-2 units) the running state is
@@ -49,7 +52,7 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     constexpr int kThreads = 64 * G;
     constexpr int kPer = (kSegs + kThreads - 1) / kThreads;
     __shared__ uint16_t kl[2][kBK * kStride];
-    __shared__ uint16_t vl[2][kBK * kStride];
+    __shared__ uint16_t vl[2][kBK * kVStride];
 
     // Work item -> (sequence b, KV head g, query block qb).  Query blocks go
     // heaviest first (the causal triangle gives late blocks the most keys).
@@ -123,9 +126,8 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
         for (int p = 0; p < kPer; ++p) {
             const int idx = threadIdx.x + p * kThreads;
             if (kSegs % kThreads == 0 || idx < kSegs) {
-                const int off = (idx / 8) * kStride + 8 * (idx % 8);
-                *reinterpret_cast<u32x4*>(&kl[buf][off]) = kreg[p];
-                *reinterpret_cast<u32x4*>(&vl[buf][off]) = vreg[p];
+                *reinterpret_cast<u32x4*>(&kl[buf][(idx / 8) * kStride + 8 * (idx % 8)]) = kreg[p];
+                *reinterpret_cast<u32x4*>(&vl[buf][(idx / 8) * kVStride + 8 * (idx % 8)]) = vreg[p];
             }
         }
     };
@@ -207,9 +209,9 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
             const int key_base = 32 * (ks / 2) + 16 * (ks % 2);
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-                const uint16_t* p0 = vt + (key_base + 4 * half + c16 / 4) * kStride + 32 * mt +
+                const uint16_t* p0 = vt + (key_base + 4 * half + c16 / 4) * kVStride + 32 * mt +
                                      16 * (g4 % 2) + 4 * (c16 % 4);
-                const bf16x8 va = concat(lds_read_tr16(p0), lds_read_tr16(p0 + 8 * kStride));
+                const bf16x8 va = concat(lds_read_tr16(p0), lds_read_tr16(p0 + 8 * kVStride));
                 o[mt] = mfma32x32x16(va, pb[ks], o[mt]);
             }
         }

@@ -177,6 +177,33 @@ def cpu_baseline(dec_wl, pre_wl, budget_s: float = 20.0):
                             f"{pre_s:.3f} s"))
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_decode_b32_kv4096_prefill_b4_s4096.md")
+TRAFFIC_SOURCES = ("gqa_attention_head_amd/csrc/common.h", "gqa_attention_head_amd/csrc/decode.hip",
+                   "gqa_attention_head_amd/csrc/prefill.hip")
+
+
+def measured_traffic():
+    """Calibrated HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE summary,
+    or None for a kernel whose sources changed since those counters were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return {}
+    h = hashlib.sha256(b"".join(open(os.path.join(ROOT, f), "rb").read()
+                                for f in TRAFFIC_SOURCES)).hexdigest()
+    m = re.search(r"traffic_source_sha256: ([0-9a-f]+)", text)
+    if not m or m.group(1) != h:
+        return {}
+    out = {}
+    for key in ("decode", "prefill"):
+        v = re.search(rf"traffic_{key}_bytes_per_launch: (\d+)", text)
+        if v:
+            out[key] = int(v.group(1))
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +232,7 @@ def main(argv=None):
             "gqa_attention_head_amd.workloads", fromlist=["x"]).causal_prefill())
 
     kernel_gbs = dec["kv_bytes"] / (dec["launch_ms_mean"] * 1e-3) / 1e9
+    traffic = measured_traffic()
     line = {
         "metric": METRIC,
         "value": round(dec["gbs"], 2),
@@ -225,7 +253,9 @@ def main(argv=None):
         "hbm_frac": round(dec["gbs"] / HBM_PEAK_GBS, 4),
         "roofline": {"kernel": "decode_split_mfma<8, fused merge>", "bound": "hbm",
                      "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(kernel_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic.get("decode"),
+                     "algorithmic_bytes": dec["kv_bytes"],
                      "launch_ms_mean": round(dec["launch_ms_mean"], 5)},
     }
     if pre is not None:
@@ -235,7 +265,7 @@ def main(argv=None):
             "roofline": {"kernel": "prefill_mfma<8>", "bound": "mfma",
                          "achieved": round(pre["tflops"], 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(pre["tflops"] / BF16_PEAK_TFLOPS, 4),
-                         "traffic": None}}
+                         "traffic": traffic.get("prefill"), "algorithmic_flops": pre["flops"]}}
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

@@ -59,7 +59,7 @@ def load_library():
                                     vp, vp]
     lib.sink_attn_decode.restype = ctypes.c_int
     lib.sink_attn_decode.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
-                                     i32, i32, f32, vp, vp, vp, vp, vp, vp, vp]
+                                     i32, i32, f32, vp, vp, vp, vp, vp, vp]
     lib.sink_attn_last_error.restype = ctypes.c_char_p
     lib.sink_attn_last_error.argtypes = []
     _lib = lib
@@ -195,22 +195,18 @@ def merge(part_m, part_d, part_acc, cu_seqlens_k, kv_chunk_size, out_dtype=None,
 
 
 class DecodeWorkspace:
-    """Caller-owned scratch of ``decode``: chunk states and per-sequence arrival counters
-    (zeroed once here; every call leaves them zero)."""
+    """Caller-owned scratch of ``decode``: the chunk states (m, d, acc) of the split pass."""
 
-    def __init__(self, batch, num_q_heads, num_kv_heads, max_num_chunks, head_dim=64,
-                 device="cuda"):
-        torch = _torch()
+    def __init__(self, batch, num_q_heads, max_num_chunks, head_dim=64, device="cuda"):
         self.max_num_chunks = int(max_num_chunks)
         self.partials = partial_buffers(batch, num_q_heads, self.max_num_chunks, head_dim, device)
-        self.counters = torch.zeros(batch * num_kv_heads, dtype=torch.int32, device=device)
 
 
 def decode(q, k, v, sinks, cu_seqlens_k, max_seqlen_k, kv_chunk_size, sm_scale,
            max_num_chunks=None, workspace=None, out=None, lse=None, return_lse=False,
            stream=None):
-    """Split-KV decode in one call (``sink_attn_decode``): split pass and merge, fused into a
-    single launch where the library supports it."""
+    """Split-KV decode in one call (``sink_attn_decode``): split pass then merge, enqueued
+    back to back on the stream."""
     torch = _torch()
     lib = load_library()
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -224,10 +220,8 @@ def decode(q, k, v, sinks, cu_seqlens_k, max_seqlen_k, kv_chunk_size, sm_scale,
         max_num_chunks = (workspace.max_num_chunks if workspace is not None
                           else max(1, -(-int(max_seqlen_k) // int(kv_chunk_size))))
     if workspace is None:
-        workspace = DecodeWorkspace(batch, q.shape[1], k.shape[1], max_num_chunks, q.shape[2],
-                                    q.device)
+        workspace = DecodeWorkspace(batch, q.shape[1], max_num_chunks, q.shape[2], q.device)
     pm, pd, pa = workspace.partials
-    _dev(workspace.counters, "counters", torch.int32)
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out", q.dtype)
@@ -238,5 +232,5 @@ def decode(q, k, v, sinks, cu_seqlens_k, max_seqlen_k, kv_chunk_size, sm_scale,
                                 _ptr(cu_seqlens_k), batch, q.shape[1], k.shape[1], q.shape[2],
                                 int(max_seqlen_k), int(kv_chunk_size), int(max_num_chunks),
                                 float(sm_scale), _ptr(pm), _ptr(pd), _ptr(pa),
-                                _ptr(workspace.counters), _ptr(out), _ptr(lse), _stream(stream)))
+                                _ptr(out), _ptr(lse), _stream(stream)))
     return (out, lse) if return_lse else out

@@ -178,28 +178,20 @@ sa_status_t sink_attn_decode(sa_dtype_t dtype, const void* q, const void* k, con
                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                              int32_t max_seqlen_k, int32_t kv_chunk_size, int32_t max_num_chunks,
                              float sm_scale, float* part_m, float* part_d, float* part_acc,
-                             int32_t* counters, void* out, float* lse, void* stream) {
+                             void* out, float* lse, void* stream) {
     sa_status_t s = check_split_args(dtype, q, k, v, sinks, cu_seqlens_k, batch, num_q_heads,
                                      num_kv_heads, head_dim, max_seqlen_k, kv_chunk_size,
                                      max_num_chunks, sm_scale, part_m, part_d, part_acc);
     if (s != SA_OK) return s;
-    if (!counters || !out) return fail(SA_EINVAL, "sink_attn_decode: null pointer argument");
+    if (!out) return fail(SA_EINVAL, "sink_attn_decode: null pointer argument");
     if ((s = check_device()) != SA_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const bool fused = dtype == SA_BF16 && sa::mfma_decode_supported(num_q_heads / num_kv_heads) &&
-                       max_num_chunks <= sa::kFusedMaxChunks;
-    hipError_t e;
-    if (fused) {
-        e = sa::launch_mfma_decode_fused(q, k, v, sinks, cu_seqlens_k, batch, num_q_heads,
-                                         num_kv_heads, kv_chunk_size, max_num_chunks, sm_scale,
-                                         part_m, part_d, part_acc, counters, out, lse, st);
-    } else {
-        e = launch_split(dtype, q, k, v, sinks, cu_seqlens_k, batch, num_q_heads, num_kv_heads,
-                         kv_chunk_size, max_num_chunks, sm_scale, part_m, part_d, part_acc, st);
-        if (e == hipSuccess)
-            e = sa::launch_merge(dtype == SA_BF16, part_m, part_d, part_acc, cu_seqlens_k,
-                                 kv_chunk_size, max_num_chunks, batch, num_q_heads, out, lse, st);
-    }
+    hipError_t e = launch_split(dtype, q, k, v, sinks, cu_seqlens_k, batch, num_q_heads,
+                                num_kv_heads, kv_chunk_size, max_num_chunks, sm_scale, part_m,
+                                part_d, part_acc, st);
+    if (e == hipSuccess)
+        e = sa::launch_merge(dtype == SA_BF16, part_m, part_d, part_acc, cu_seqlens_k,
+                             kv_chunk_size, max_num_chunks, batch, num_q_heads, out, lse, st);
     return finish_launch(e, st, "sink_attn_decode");
 }
 

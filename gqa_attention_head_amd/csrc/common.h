@@ -33,12 +33,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Value held by lane (l ^ 32), via the gfx950 cross-half lane swap.
-__device__ __forceinline__ float xor32(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    // lanes < 32 get (x[l], x[l+32]); lanes >= 32 get (x[l-32], x[l]).
-    return __uint_as_float((__lane_id() < 32) ? r[1] : r[0]);
-}
+// Cross-half (lane l and l ^ 32) max and sum, via the gfx950 lane swap: lanes < 32
+// receive (x[l], x[l+32]), lanes >= 32 receive (x[l-32], x[l]).
 __device__ __forceinline__ float max_xor32(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -77,42 +73,9 @@ __device__ __forceinline__ u32x4 load_stream(const uint16_t* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-// Device-scope coherent float store/load (relaxed): visible to workgroups on
-// every XCD without flushing or invalidating the per-XCD L2 caches.
-__device__ __forceinline__ void store_coherent(float* p, float x) {
-    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_coherent(const float* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// 16-byte device-coherent loads and stores of a float array through a buffer
-// resource (cache policy SC1, the same bit the device-scope atomics above use).
-struct CoherentBuffer {
-    static constexpr int kSC1 = 16;                  // cache-policy bit of the access
-    static constexpr unsigned kRawDword3 = 0x00020000u;
-    __amdgpu_buffer_rsrc_t rsrc;
-    __device__ CoherentBuffer(float* base, int n_floats)
-        : rsrc(__builtin_amdgcn_make_buffer_rsrc(base, 0, n_floats * 4, kRawDword3)) {}
-    __device__ void store4(int idx, f32x4 x) const {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), rsrc, idx * 4, 0, kSC1);
-    }
-    __device__ f32x4 load4(int idx) const {
-        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, idx * 4, 0, kSC1));
-    }
-};
-
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
-
-// Direct global->LDS copy of 16 bytes per lane (gfx950): lane l's bytes land at
-// lds_base + 16*l; lds_base must be the same for the whole wave.  The compiler
-// does not track these writes: wait_dma() must precede any read of the data.
-__device__ __forceinline__ void lds_dma16(const uint16_t* src, uint16_t* lds_base) {
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Orders this wave's earlier LDS writes before its later LDS reads (in-order LDS
 // queue + compiler barrier); used where a wave hands data between its own lanes.

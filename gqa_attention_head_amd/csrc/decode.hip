@@ -15,8 +15,6 @@
 // DRAM row that another workgroup reads later.  Each wave keeps kDepth tiles
 // of loads in flight in registers, read with nontemporal loads.
 //
-// The one-call variant (kFused) also combines the chunk states: the last
-// workgroup to finish a (sequence, head block) merges them.
 //
 // Per 32-key tile and wave:
 //   S^T[32 keys x 16 heads] = K[32 x 64] . Q^T[64 x 16]      4 MFMA 16x16x32
@@ -122,15 +120,13 @@ __device__ __forceinline__ void process_tile(WaveState& st, const DecodeTile& cu
     }
 }
 
-template <int G, int kDepth, int kHeadsPerBlock, bool kFused>
+template <int G, int kDepth, int kHeadsPerBlock>
 __global__ __launch_bounds__(64 * kHeadsPerBlock) void decode_split_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ sinks,
     const int32_t* __restrict__ cu_k, int hq, int hkv, int chunk, int max_chunks,
     int head_blocks, float scale_log2, float* __restrict__ part_m,
-    float* __restrict__ part_d, float* __restrict__ part_acc, int32_t* __restrict__ counters,
-    uint16_t* __restrict__ out, float* __restrict__ lse) {
-    constexpr int kThreads = 64 * kHeadsPerBlock;
+    float* __restrict__ part_d, float* __restrict__ part_acc) {
     __shared__ uint16_t vlds[kHeadsPerBlock][kTile * kVStride];
 
     // blockIdx -> (b, chunk c, head block hb), head block fastest
@@ -205,143 +201,30 @@ __global__ __launch_bounds__(64 * kHeadsPerBlock) void decode_split_mfma(
 
     const float m_nat = (st.m == kNegInf) ? kNegInf : st.m * kLn2;
     const int64_t slot = ((int64_t)b * hq + h) * max_chunks + c;
-    if (!kFused) {
-        if (head_ok) {
-            float* pa = part_acc + slot * kD;
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) *reinterpret_cast<f32x4*>(pa + 16 * mt + 4 * q4) = st.o[mt];
-            if (q4 == 0) {
-                part_m[slot] = m_nat;
-                part_d[slot] = st.dl;
-            }
-        }
-        return;
-    }
-
-    // ---- one-call variant: publish the state, count arrivals, merge in the last.
-    // States go out with device-coherent stores (past the per-XCD L2), each wave
-    // waits for its stores to complete, and one arrival per workgroup is counted;
-    // the last arrival reads every state with device-coherent loads.
-    const int hbase = hb * kHeadsPerBlock * G;             // first query head of the block
-    const int nh = min(kHeadsPerBlock, hkv - hb * kHeadsPerBlock) * G;
-    const int64_t blk_states = ((int64_t)b * hq + hbase) * max_chunks;
-    const CoherentBuffer acc_buf(part_acc + blk_states * kD, nh * max_chunks * kD);
     if (head_ok) {
-        const int off = ((h - hbase) * max_chunks + c) * kD;
+        float* pa = part_acc + slot * kD;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc_buf.store4(off + 16 * mt + 4 * q4, st.o[mt]);
+        for (int mt = 0; mt < 4; ++mt) *reinterpret_cast<f32x4*>(pa + 16 * mt + 4 * q4) = st.o[mt];
         if (q4 == 0) {
-            store_coherent(part_m + slot, m_nat);
-            store_coherent(part_d + slot, st.dl);
+            part_m[slot] = m_nat;
+            part_d[slot] = st.dl;
         }
     }
-    __shared__ int s_last;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    int32_t* counter = counters + (int64_t)b * head_blocks + hb;
-    if (threadIdx.x == 0)
-        s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                 nch - 1;
-    __syncthreads();
-    if (!s_last) return;
-
-    // Merge of the nch chunk states of every head in the block.  All loads of a
-    // phase are issued before any is used.
-    constexpr int kMaxSlots = kFusedMaxChunks;
-    constexpr int kHeads = kHeadsPerBlock * G;
-    __shared__ float s_m[kHeads][kMaxSlots];
-    __shared__ float s_w[kHeads][kMaxSlots];
-    __shared__ float s_d[kHeads][kMaxSlots];
-    __shared__ float s_big[kHeads], s_den[kHeads];
-    const int nslots = nch;
-    constexpr int kPerA = ceil_div(kHeads * kMaxSlots, kThreads);
-    float mv[kPerA], dv[kPerA];
-#pragma unroll
-    for (int p = 0; p < kPerA; ++p) {
-        const int idx = threadIdx.x + p * kThreads;
-        const int hl = idx / kMaxSlots, sl = idx % kMaxSlots;
-        const bool ok = hl < nh && sl < nslots;
-        const int64_t at = blk_states + (int64_t)hl * max_chunks + sl;
-        mv[p] = ok ? load_coherent(part_m + at) : kNegInf;
-        dv[p] = ok ? load_coherent(part_d + at) : 0.0f;
-    }
-#pragma unroll
-    for (int p = 0; p < kPerA; ++p) {
-        const int idx = threadIdx.x + p * kThreads;
-        if (idx < kHeads * kMaxSlots) {
-            s_m[idx / kMaxSlots][idx % kMaxSlots] = mv[p];
-            s_d[idx / kMaxSlots][idx % kMaxSlots] = dv[p];
-        }
-    }
-    __syncthreads();
-    for (int hl = threadIdx.x; hl < nh; hl += kThreads) {
-        float big = kNegInf;
-        for (int sl = 0; sl < nslots; ++sl) big = fmaxf(big, s_m[hl][sl]);
-        float den = 0.0f;
-        for (int sl = 0; sl < kMaxSlots; ++sl) {
-            const float mc = s_m[hl][sl];
-            const float w = (big == kNegInf || mc == kNegInf) ? 0.0f : fast_exp2((mc - big) * kLog2e);
-            s_w[hl][sl] = w;
-            den += w * s_d[hl][sl];
-        }
-        s_big[hl] = big;
-        s_den[hl] = den;
-    }
-    __syncthreads();
-    for (int item = threadIdx.x; item < nh * (kD / 4); item += kThreads) {
-        const int hl = item / (kD / 4), qd = item % (kD / 4);
-        f32x4 a[kMaxSlots];
-#pragma unroll
-        for (int sl = 0; sl < kMaxSlots; ++sl)
-            a[sl] = (sl < nslots) ? acc_buf.load4((hl * max_chunks + sl) * kD + 4 * qd)
-                                  : f32x4{0.f, 0.f, 0.f, 0.f};
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int sl = 0; sl < kMaxSlots; ++sl) acc += s_w[hl][sl] * a[sl];
-        const float big = s_big[hl], den = s_den[hl];
-        const bool empty = (big == kNegInf) || !(den > 0.0f);
-        const float inv = empty ? 0.0f : 1.0f / den;
-        const uint32_t lo2 = (uint32_t)f32_to_bf16_bits(acc[0] * inv) |
-                             ((uint32_t)f32_to_bf16_bits(acc[1] * inv) << 16);
-        const uint32_t hi2 = (uint32_t)f32_to_bf16_bits(acc[2] * inv) |
-                             ((uint32_t)f32_to_bf16_bits(acc[3] * inv) << 16);
-        *reinterpret_cast<u32x2*>(out + ((int64_t)b * hq + hbase + hl) * kD + 4 * qd) = u32x2{lo2, hi2};
-        if (lse != nullptr && qd == 0)
-            lse[(int64_t)b * hq + hbase + hl] = empty ? kNegInf : big + fast_log2(den) * kLn2;
-    }
-    // ready for the next call (stream order makes it visible to the next launch)
-    if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int G, bool kFused>
+template <int G>
 hipError_t launch_g(const void* q, const void* k, const void* v, const float* sinks,
                     const int32_t* cu_k, int batch, int hq, int hkv, int chunk, int max_chunks,
                     float sm_scale, float* part_m, float* part_d, float* part_acc,
-                    int32_t* counters, void* out, float* lse, hipStream_t stream) {
+                    hipStream_t stream) {
     constexpr int kDepth = 2, kHeadsPerBlock = 8;
     const int head_blocks = ceil_div(hkv, kHeadsPerBlock);
     const int64_t blocks = (int64_t)batch * max_chunks * head_blocks;
-    hipLaunchKernelGGL((decode_split_mfma<G, kDepth, kHeadsPerBlock, kFused>),
-                       dim3((unsigned)blocks), dim3(64 * kHeadsPerBlock), 0, stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, sinks, cu_k, hq,
-                       hkv, chunk, max_chunks, head_blocks, sm_scale * kLog2e, part_m, part_d,
-                       part_acc, counters, (uint16_t*)out, lse);
+    hipLaunchKernelGGL((decode_split_mfma<G, kDepth, kHeadsPerBlock>), dim3((unsigned)blocks),
+                       dim3(64 * kHeadsPerBlock), 0, stream, (const uint16_t*)q, (const uint16_t*)k,
+                       (const uint16_t*)v, sinks, cu_k, hq, hkv, chunk, max_chunks, head_blocks,
+                       sm_scale * kLog2e, part_m, part_d, part_acc);
     return hipGetLastError();
-}
-
-template <bool kFused>
-hipError_t dispatch(const void* q, const void* k, const void* v, const float* sinks,
-                    const int32_t* cu_k, int batch, int hq, int hkv, int chunk, int max_chunks,
-                    float sm_scale, float* part_m, float* part_d, float* part_acc,
-                    int32_t* counters, void* out, float* lse, hipStream_t stream) {
-    switch (hq / hkv) {
-        case 1: return launch_g<1, kFused>(q, k, v, sinks, cu_k, batch, hq, hkv, chunk, max_chunks, sm_scale, part_m, part_d, part_acc, counters, out, lse, stream);
-        case 2: return launch_g<2, kFused>(q, k, v, sinks, cu_k, batch, hq, hkv, chunk, max_chunks, sm_scale, part_m, part_d, part_acc, counters, out, lse, stream);
-        case 4: return launch_g<4, kFused>(q, k, v, sinks, cu_k, batch, hq, hkv, chunk, max_chunks, sm_scale, part_m, part_d, part_acc, counters, out, lse, stream);
-        case 8: return launch_g<8, kFused>(q, k, v, sinks, cu_k, batch, hq, hkv, chunk, max_chunks, sm_scale, part_m, part_d, part_acc, counters, out, lse, stream);
-        case 16: return launch_g<16, kFused>(q, k, v, sinks, cu_k, batch, hq, hkv, chunk, max_chunks, sm_scale, part_m, part_d, part_acc, counters, out, lse, stream);
-        default: return hipErrorInvalidValue;
-    }
 }
 
 }  // namespace
@@ -355,17 +238,14 @@ hipError_t launch_mfma_decode_split(const void* q, const void* k, const void* v,
                                     int hkv, int chunk, int max_chunks, float sm_scale,
                                     float* part_m, float* part_d, float* part_acc,
                                     hipStream_t stream) {
-    return dispatch<false>(q, k, v, sinks, cu_k, batch, hq, hkv, chunk, max_chunks, sm_scale,
-                              part_m, part_d, part_acc, nullptr, nullptr, nullptr, stream);
-}
-
-hipError_t launch_mfma_decode_fused(const void* q, const void* k, const void* v,
-                                    const float* sinks, const int32_t* cu_k, int batch, int hq,
-                                    int hkv, int chunk, int max_chunks, float sm_scale,
-                                    float* part_m, float* part_d, float* part_acc,
-                                    int32_t* counters, void* out, float* lse, hipStream_t stream) {
-    return dispatch<true>(q, k, v, sinks, cu_k, batch, hq, hkv, chunk, max_chunks, sm_scale,
-                          part_m, part_d, part_acc, counters, out, lse, stream);
+    switch (hq / hkv) {
+        case 1: return launch_g<1>(q, k, v, sinks, cu_k, batch, hq, hkv, chunk, max_chunks, sm_scale, part_m, part_d, part_acc, stream);
+        case 2: return launch_g<2>(q, k, v, sinks, cu_k, batch, hq, hkv, chunk, max_chunks, sm_scale, part_m, part_d, part_acc, stream);
+        case 4: return launch_g<4>(q, k, v, sinks, cu_k, batch, hq, hkv, chunk, max_chunks, sm_scale, part_m, part_d, part_acc, stream);
+        case 8: return launch_g<8>(q, k, v, sinks, cu_k, batch, hq, hkv, chunk, max_chunks, sm_scale, part_m, part_d, part_acc, stream);
+        case 16: return launch_g<16>(q, k, v, sinks, cu_k, batch, hq, hkv, chunk, max_chunks, sm_scale, part_m, part_d, part_acc, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace sa

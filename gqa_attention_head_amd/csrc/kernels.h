@@ -24,16 +24,6 @@ hipError_t launch_mfma_decode_split(const void* q, const void* k, const void* v,
                                     int hkv, int chunk, int max_chunks, float sm_scale,
                                     float* part_m, float* part_d, float* part_acc,
                                     hipStream_t stream);
-// Split pass and merge in one launch (bf16 output); the last workgroup to finish a
-// (sequence, block of 8 KV heads) merges its chunk states (max_chunks <=
-// kFusedMaxChunks).  counters: one int per (sequence, head block), zero on entry,
-// left zero.
-constexpr int kFusedMaxChunks = 16;
-hipError_t launch_mfma_decode_fused(const void* q, const void* k, const void* v,
-                                    const float* sinks, const int32_t* cu_k, int batch, int hq,
-                                    int hkv, int chunk, int max_chunks, float sm_scale,
-                                    float* part_m, float* part_d, float* part_acc,
-                                    int32_t* counters, void* out, float* lse, hipStream_t stream);
 bool mfma_prefill_supported(int group);
 hipError_t launch_mfma_prefill(const void* q, const void* k, const void* v, const float* sinks,
                                const int32_t* cu_q, const int32_t* cu_k, int batch, int hq,

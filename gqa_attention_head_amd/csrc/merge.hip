@@ -8,9 +8,9 @@
 // lse = M + ln sum_c w_c d_c.  The sink already sits in chunk 0's state.
 //
 // One wave per (sequence, query head); lane = output dimension (head_dim 64).
-// The wave first finds M (lanes stride over the chunks), then each lane
-// computes the weight of one chunk and the lanes sweep the chunks' rows for
-// their own dimension, the weights broadcast across the wave.
+// The chunk states are read in groups of kGroup chunks, every load of a group
+// issued before any is used (a single round trip for up to kGroup chunks); a
+// later group, if any, folds in with the usual rescale of the running sums.
 #include "common.h"
 #include "kernels.h"
 
@@ -20,6 +20,7 @@ namespace {
 
 constexpr int kD = 64;
 constexpr int kWavesPerBlock = 4;
+constexpr int kGroup = 16;  // chunk states loaded per round trip
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -42,37 +43,51 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void merge_kernel(
     const int pair = blockIdx.x * kWavesPerBlock + wave;
     if (pair >= batch * hq) return;  // no workgroup barrier below
     const int b = pair / hq;
-    const int len = cu_k[b + 1] - cu_k[b];
-    const int nch = min(max_chunks, max(1, ceil_div(len, chunk)));
     const int64_t base = (int64_t)pair * max_chunks;
 
-    float big = kNegInf;
-    for (int c = lane; c < nch; c += 64) big = fmaxf(big, part_m[base + c]);
-    big = wave_max(big);
+    // The first group's loads do not wait for the sequence length: they read
+    // slots clamped to the buffer's last one and are masked once nch is known.
+    const int k_lo = cu_k[b], k_hi = cu_k[b + 1];
+    float m_ld, d_ld, av[kGroup];
+    auto load_group = [&](int c0) {
+        // lane u < kGroup: chunk c0 + u's m and d; every lane: its dimension of
+        // the kGroup accumulators
+        const int cl = min(c0 + lane % kGroup, max_chunks - 1);
+        m_ld = part_m[base + cl];
+        d_ld = part_d[base + cl];
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u)
+            av[u] = part_acc[(base + min(c0 + u, max_chunks - 1)) * kD + lane];
+    };
+    load_group(0);
+    __builtin_amdgcn_sched_barrier(0);
+    const int nch = min(max_chunks, max(1, ceil_div(k_hi - k_lo, chunk)));
 
-    float acc = 0.0f, den = 0.0f;
-    if (big != kNegInf) {
-        for (int c0 = 0; c0 < nch; c0 += 64) {
-            // lane j of the group holds chunk c0 + j's weight
-            const int c = c0 + lane;
-            float w = 0.0f, dw = 0.0f;
-            if (c < nch) {
-                const float mc = part_m[base + c];
-                w = (mc == kNegInf) ? 0.0f : fast_exp2((mc - big) * kLog2e);
-                dw = w * part_d[base + c];
+    float big = kNegInf, acc = 0.0f, den = 0.0f;
+    for (int c0 = 0;;) {
+        const bool mine = lane < kGroup && c0 + lane < nch;
+        const float ml = mine ? m_ld : kNegInf;
+        const float nbig = fmaxf(big, wave_max(ml));
+        if (nbig != kNegInf) {  // (uniform) otherwise nothing finite yet
+            if (nbig != big) {
+                const float scale = (big == kNegInf) ? 0.0f : fast_exp2((big - nbig) * kLog2e);
+                acc *= scale;
+                den *= scale;
+                big = nbig;
             }
-            den += wave_sum(dw);
-            const int n = min(64, nch - c0);
-            // lane = output dimension; eight chunk rows in flight at a time
-            for (int j0 = 0; j0 < n; j0 += 8) {
-                float vals[8];
+            const float wl = (ml == kNegInf) ? 0.0f : fast_exp2((ml - big) * kLog2e);
+            den += wave_sum(mine ? wl * d_ld : 0.0f);
 #pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    vals[u] = (j0 + u < n) ? part_acc[(base + c0 + j0 + u) * kD + lane] : 0.0f;
-#pragma unroll
-                for (int u = 0; u < 8; ++u) acc += __shfl(w, j0 + u) * vals[u];
+            for (int u = 0; u < kGroup; ++u) {
+                // chunk c0 + u's weight, from lane u (0 for chunks past the end,
+                // whose slots may hold anything: select, do not multiply)
+                const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));
+                acc += (w != 0.0f) ? w * av[u] : 0.0f;
             }
         }
+        c0 += kGroup;
+        if (c0 >= nch) break;
+        load_group(c0);
     }
     const bool empty = (big == kNegInf) || !(den > 0.0f);
     const float o = empty ? 0.0f : acc / den;

@@ -134,27 +134,21 @@ sa_status_t sink_attn_merge(sa_dtype_t out_dtype, const float *part_m, const flo
                             void *stream);
 
 /*
- * Split-KV decode in one call: the first pass and the log-sum-exp combination
- * above (same arguments, same partial states, same result), issued as a single
- * launch when the work allows it: bf16 with Hq/Hkv in {1, 2, 4, 8, 16} and at
- * most 16 chunks per sequence.  There the last workgroup to finish a sequence's
- * chunks combines them, which needs a small arrival counter per sequence.
- * Otherwise the call runs the two passes back to back on `stream`.
+ * Split-KV decode in one call: sink_attn_decode_split then sink_attn_merge,
+ * enqueued back to back on `stream` (same arguments, same partial states, same
+ * result as calling the two).
  *
  *   part_m, part_d, part_acc  caller-owned workspace, laid out as for
- *             sink_attn_decode_split (their contents after the call are unspecified).
- *   counters  [batch * Hkv] int32 caller-owned workspace; all zero before the
- *             first call, and every call leaves it all zero again.  Calls that
- *             share a counters array must not run concurrently (stream order is
- *             enough).
+ *             sink_attn_decode_split (they hold the chunk states after the call).
  *   out       [batch, Hq, D] dtype;  lse nullable [batch, Hq] float32.
+ * Errors: those of sink_attn_decode_split, and SA_EINVAL for a null `out`.
  */
 sa_status_t sink_attn_decode(sa_dtype_t dtype, const void *q, const void *k, const void *v,
                              const float *sinks, const int32_t *cu_seqlens_k, int32_t batch,
                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                              int32_t max_seqlen_k, int32_t kv_chunk_size, int32_t max_num_chunks,
                              float sm_scale, float *part_m, float *part_d, float *part_acc,
-                             int32_t *counters, void *out, float *lse, void *stream);
+                             void *out, float *lse, void *stream);
 
 /* Text of the calling thread's last non-OK status ("" if none).  Valid until the next call. */
 const char *sink_attn_last_error(void);

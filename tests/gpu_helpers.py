@@ -120,9 +120,9 @@ def assert_lse_close(got, want, bf16: bool):
         assert err <= tol, f"lse: max abs err {err:.3e} > {tol}"
 
 
-def run_decode_fused(dev: Device, chunk: int, q=None, cu_k=None, max_lk=None, workspace=None,
+def run_decode_call(dev: Device, chunk: int, q=None, cu_k=None, max_lk=None, workspace=None,
                      max_num_chunks=None):
-    """One ``sink_attn_decode`` call (fused split + merge where supported)."""
+    """One ``sink_attn_decode`` call (split pass and merge enqueued together)."""
     wl = dev.wl
     q = dev.q if q is None else q
     cu_k = dev.cu_k if cu_k is None else cu_k

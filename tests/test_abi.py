@@ -75,8 +75,7 @@ def _split(lib, **kw):
 
 def _decode(lib, **kw):
     a = dict(dtype=sa.SA_BF16, q=P, k=P, v=P, sinks=P, cu_k=P, batch=2, hq=64, hkv=8, d=64,
-             max_k=4096, chunk=512, max_chunks=8, scale=0.125, pm=P, pd=P, pa=P, counters=P,
-             out=P, lse=NULL, stream=NULL)
+             max_k=4096, chunk=512, max_chunks=8, scale=0.125, pm=P, pd=P, pa=P, out=P, lse=NULL, stream=NULL)
     a.update(kw)
     return lib.sink_attn_decode(*a.values())
 
@@ -124,7 +123,6 @@ def test_decode_split_rejects(lib, kw, status):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(counters=NULL), sa.SA_EINVAL),
     (dict(out=NULL), sa.SA_EINVAL),
     (dict(pm=NULL), sa.SA_EINVAL),
     (dict(max_chunks=7), sa.SA_EINVAL),

@@ -95,12 +95,23 @@ def bench_decode(steps: int, warmup: int):
         step(i)
     _sync()
     wall2 = time.perf_counter() - t0
+    # The same step replayed from captured HIP graphs (one per K/V copy).
+    graphs = [sa.DecodeGraph(q, ks[j], vs[j], sinks, cu_k, max_lk, chunk, wl.sm_scale, out=out,
+                             lse=lse) for j in range(KV_COPIES)]
+    for i in range(warmup):
+        graphs[i % KV_COPIES].replay()
+    _sync()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % KV_COPIES].replay()
+    _sync()
+    graph_ms = (time.perf_counter() - t0) * 1e3 / steps
     kv_bytes = wl.kv_bytes()
     ms_per_step = wall2 * 1e3 / steps
     return dict(
         workload=wl.name, kv_bytes=kv_bytes, ms_per_step=ms_per_step,
         gbs=kv_bytes / (ms_per_step * 1e-3) / 1e9,
-        split_ms_mean=float(split_ms),
+        split_ms_mean=float(split_ms), graph_ms_per_step=graph_ms,
         batch=wl.batch, kv_len=int(max_lk), chunk=chunk, num_chunks=nch, wl=wl)
 
 
@@ -255,6 +266,9 @@ def main(argv=None):
                    "kv_chunk": dec["chunk"], "num_chunks": dec["num_chunks"],
                    "kv_copies_rotated": KV_COPIES, "parallelism": "single-gpu"},
         "hbm_frac": round(dec["gbs"] / HBM_PEAK_GBS, 4),
+        "graph_replay": {"ms_per_step": round(dec["graph_ms_per_step"], 5),
+                         "value": round(dec["kv_bytes"] / (dec["graph_ms_per_step"] * 1e-3) / 1e9, 2),
+                         "unit": "GB/s"},
         "roofline": {"kernel": "decode_split_mfma<8>", "bound": "hbm",
                      "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),

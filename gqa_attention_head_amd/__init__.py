@@ -234,3 +234,46 @@ def decode(q, k, v, sinks, cu_seqlens_k, max_seqlen_k, kv_chunk_size, sm_scale,
                                 float(sm_scale), _ptr(pm), _ptr(pd), _ptr(pa),
                                 _ptr(out), _ptr(lse), _stream(stream)))
     return (out, lse) if return_lse else out
+
+
+class DecodeGraph:
+    """One ``decode`` call (split pass + merge) captured as a HIP graph and replayed.
+
+    The pages' serving engine runs its decode step under graph capture; here the
+    two launches of a decode call are recorded once (torch.cuda.CUDAGraph on a
+    default-priority capture stream) and ``replay()`` re-runs them on the current
+    stream.  Every buffer is fixed at capture: q, k, v, sinks, cu_seqlens_k, the
+    workspace and the outputs.  Write new inputs into those tensors in place
+    (``copy_``) before a replay; the lengths in cu_seqlens_k may change between
+    replays as long as they stay within ``max_seqlen_k`` and the workspace.
+    Nothing in the captured work is a memset, so replays need no re-zeroing.
+    """
+
+    def __init__(self, q, k, v, sinks, cu_seqlens_k, max_seqlen_k, kv_chunk_size, sm_scale,
+                 max_num_chunks=None, out=None, lse=None):
+        torch = _torch()
+        batch = cu_seqlens_k.numel() - 1
+        if max_num_chunks is None:
+            max_num_chunks = max(1, -(-int(max_seqlen_k) // int(kv_chunk_size)))
+        self.workspace = DecodeWorkspace(batch, q.shape[1], max_num_chunks, q.shape[2], q.device)
+        self.out = torch.empty_like(q) if out is None else out
+        self.lse = (torch.empty(batch, q.shape[1], device=q.device, dtype=torch.float32)
+                    if lse is None else lse)
+        args = (q, k, v, sinks, cu_seqlens_k, max_seqlen_k, kv_chunk_size, sm_scale)
+        kw = dict(max_num_chunks=max_num_chunks, workspace=self.workspace, out=self.out,
+                  lse=self.lse)
+        # one eager call first (argument checks, library load) on a side stream
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            decode(*args, **kw)
+        torch.cuda.current_stream().wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            decode(*args, **kw)
+        self._keep = args  # the captured pointers must stay alive
+
+    def replay(self):
+        """Run the captured decode on the current stream; returns ``(out, lse)``."""
+        self.graph.replay()
+        return self.out, self.lse

@@ -272,3 +272,35 @@ def test_decode_call_empty_sequences(orc):
     ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
     H.assert_close(out, ref, bf16=True)
     H.assert_lse_close(lse, ref_lse, bf16=True)
+
+
+# ---------------------------------------------------------------- graph-captured decode
+
+def test_decode_graph_replays(orc):
+    """A captured decode call replayed several times, with eager work and host
+    synchronisation between replays: every replay equals the eager call bit for bit,
+    also after new inputs are copied into the captured buffers."""
+    wl = W.random_case(91, batch=6, hq=16, hkv=2, max_k=2500, decode=True,
+                       sink_values=[-np.inf, 20.0, -20.0, 0.5] * 4)
+    dev = H.Device(wl)
+    chunk = 512
+    g = sa.DecodeGraph(dev.q, dev.k, dev.v, dev.sinks, dev.cu_k, dev.max_lk, chunk, wl.sm_scale)
+    eager = sa.decode(dev.q, dev.k, dev.v, dev.sinks, dev.cu_k, dev.max_lk, chunk, wl.sm_scale,
+                      return_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    H.assert_close(eager[0].float().cpu().numpy().astype(np.float64), ref, bf16=True)
+    for i in range(3):
+        out, lse = g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager[0]) and torch.equal(lse, eager[1]), f"replay {i} differs"
+        _ = (torch.randn(1024, device="cuda") * 2).sum().item()  # eager work in between
+    # new queries written into the captured buffer
+    q2 = torch.flip(dev.q, dims=[0]).contiguous()
+    dev.q.copy_(q2)
+    eager2 = sa.decode(dev.q, dev.k, dev.v, dev.sinks, dev.cu_k, dev.max_lk, chunk, wl.sm_scale,
+                       return_lse=True)
+    for i in range(2):
+        out, lse = g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager2[0]) and torch.equal(lse, eager2[1]), f"replay {i} (new q)"

@@ -21,7 +21,8 @@ LIBRARY = os.path.join(PKG, "libsinkattn.so")
 SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_ELAUNCH = 0, 1, 2, 3
 SA_FP32, SA_BF16 = 0, 1
 EXPORTS = ("sink_attn_prefill", "sink_attn_decode_split", "sink_attn_merge",
-           "sink_attn_decode", "sink_attn_last_error")
+           "sink_attn_decode", "sink_attn_prefill_split", "sink_attn_merge_rows",
+           "sink_attn_last_error")
 
 
 class SinkAttnError(RuntimeError):
@@ -60,6 +61,11 @@ def load_library():
     lib.sink_attn_decode.restype = ctypes.c_int
     lib.sink_attn_decode.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                      i32, i32, f32, vp, vp, vp, vp, vp, vp]
+    lib.sink_attn_prefill_split.restype = ctypes.c_int
+    lib.sink_attn_prefill_split.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                            i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp]
+    lib.sink_attn_merge_rows.restype = ctypes.c_int
+    lib.sink_attn_merge_rows.argtypes = [ctypes.c_int, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.sink_attn_last_error.restype = ctypes.c_char_p
     lib.sink_attn_last_error.argtypes = []
     _lib = lib
@@ -135,6 +141,58 @@ def prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen
                                  q.shape[1], k.shape[1], q.shape[2], int(max_seqlen_q),
                                  int(max_seqlen_k), float(sm_scale), int(bool(causal)), _ptr(out),
                                  _ptr(lse), _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def prefill_split(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                  kv_chunk_size, sm_scale, causal=True, max_num_chunks=None, partials=None,
+                  stream=None):
+    """Split-KV prefill first pass (``sink_attn_prefill_split``): per (row, head, chunk)
+    states; returns (part_m, part_d, part_acc) with rows indexing q's rows."""
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name, q.dtype)
+    _dev(sinks, "sinks", torch.float32)
+    _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or k.shape != v.shape:
+        raise ValueError("q must be [total_q, Hq, D]; k and v [total_k, Hkv, D]")
+    if max_num_chunks is None:
+        max_num_chunks = max(1, -(-int(max_seqlen_k) // int(kv_chunk_size)))
+    if partials is None:
+        partials = partial_buffers(q.shape[0], q.shape[1], max_num_chunks, q.shape[2], q.device)
+    pm, pd, pa = partials
+    for name, t in (("part_m", pm), ("part_d", pd), ("part_acc", pa)):
+        _dev(t, name, torch.float32)
+    _check(lib.sink_attn_prefill_split(
+        _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(cu_seqlens_q),
+        _ptr(cu_seqlens_k), cu_seqlens_q.numel() - 1, q.shape[1], k.shape[1], q.shape[2],
+        int(max_seqlen_q), int(max_seqlen_k), int(kv_chunk_size), int(max_num_chunks),
+        float(sm_scale), int(bool(causal)), _ptr(pm), _ptr(pd), _ptr(pa), _stream(stream)))
+    return pm, pd, pa
+
+
+def merge_rows(part_m, part_d, part_acc, out_dtype=None, out=None, lse=None, return_lse=False,
+               stream=None):
+    """Log-sum-exp combination of every slot of per-row chunk states
+    (``sink_attn_merge_rows``); returns out [rows, Hq, D] (and lse [rows, Hq])."""
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("part_m", part_m), ("part_d", part_d), ("part_acc", part_acc)):
+        _dev(t, name, torch.float32)
+    rows, hq, nch = part_m.shape
+    d = part_acc.shape[-1]
+    if out is None:
+        out = torch.empty(rows, hq, d, device=part_m.device,
+                          dtype=out_dtype if out_dtype is not None else torch.float32)
+    _dev(out, "out")
+    if lse is None and return_lse:
+        lse = torch.empty(rows, hq, device=part_m.device, dtype=torch.float32)
+    _dev(lse, "lse", torch.float32)
+    _check(lib.sink_attn_merge_rows(_dtype_code(out), _ptr(part_m), _ptr(part_d),
+                                    _ptr(part_acc), rows, hq, d, nch, _ptr(out), _ptr(lse),
+                                    _stream(stream)))
     return (out, lse) if return_lse else out
 
 

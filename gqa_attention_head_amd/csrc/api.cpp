@@ -110,6 +110,77 @@ sa_status_t sink_attn_prefill(sa_dtype_t dtype, const void* q, const void* k, co
     return finish_launch(e, st, "sink_attn_prefill");
 }
 
+sa_status_t sink_attn_prefill_split(sa_dtype_t dtype, const void* q, const void* k, const void* v,
+                                    const float* sinks, const int32_t* cu_seqlens_q,
+                                    const int32_t* cu_seqlens_k, int32_t batch,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                    int32_t kv_chunk_size, int32_t max_num_chunks, float sm_scale,
+                                    int32_t causal, float* part_m, float* part_d, float* part_acc,
+                                    void* stream) {
+    sa_status_t s;
+    if ((s = check_dtype(dtype)) != SA_OK) return s;
+    if (!q || !k || !v || !sinks || !cu_seqlens_q || !cu_seqlens_k || !part_m || !part_d ||
+        !part_acc)
+        return fail(SA_EINVAL, "sink_attn_prefill_split: null pointer argument");
+    if ((s = check_heads(batch, num_q_heads, num_kv_heads, head_dim)) != SA_OK) return s;
+    if (max_seqlen_q < 0 || max_seqlen_k < 0)
+        return fail(SA_EINVAL, "max_seqlen_q/max_seqlen_k must be >= 0");
+    if (causal != 0 && causal != 1) return fail(SA_EINVAL, "causal must be 0 or 1");
+    if (kv_chunk_size < 1) return fail(SA_EINVAL, "kv_chunk_size must be >= 1, got %d", kv_chunk_size);
+    const int64_t need = max_seqlen_k == 0 ? 1 : ((int64_t)max_seqlen_k + kv_chunk_size - 1) / kv_chunk_size;
+    if (max_num_chunks < need)
+        return fail(SA_EINVAL, "max_num_chunks (%d) < ceil(max_seqlen_k / kv_chunk_size) = %lld",
+                    max_num_chunks, (long long)need);
+    if (!(std::isfinite(sm_scale) && sm_scale > 0.0f))
+        return fail(SA_EINVAL, "sm_scale must be finite and > 0");
+    const int group = num_q_heads / num_kv_heads;
+    const bool mfma = dtype == SA_BF16 && sa::mfma_prefill_supported(group);
+    if (mfma) {
+        if ((int64_t)batch * num_kv_heads * ((max_seqlen_q + 31) / 32) * max_num_chunks > 0x7fffffffLL)
+            return fail(SA_EINVAL, "batch * Hkv * query blocks * max_num_chunks exceeds the grid limit");
+    } else if ((int64_t)batch * max_num_chunks > 65535) {
+        return fail(SA_EINVAL, "batch * max_num_chunks must be <= 65535 on this path");
+    }
+    if (max_seqlen_q == 0) return ok();
+    if ((s = check_device()) != SA_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (mfma)
+        e = sa::launch_mfma_prefill_split(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, batch,
+                                          num_q_heads, num_kv_heads, max_seqlen_q, kv_chunk_size,
+                                          max_num_chunks, sm_scale, causal, nullptr, nullptr,
+                                          part_m, part_d, part_acc, st);
+    else
+        e = sa::launch_generic_prefill_split(dtype == SA_BF16, q, k, v, sinks, cu_seqlens_q,
+                                             cu_seqlens_k, batch, num_q_heads, num_kv_heads,
+                                             max_seqlen_q, kv_chunk_size, max_num_chunks, sm_scale,
+                                             causal, part_m, part_d, part_acc, st);
+    return finish_launch(e, st, "sink_attn_prefill_split");
+}
+
+sa_status_t sink_attn_merge_rows(sa_dtype_t out_dtype, const float* part_m, const float* part_d,
+                                 const float* part_acc, int32_t num_rows, int32_t num_q_heads,
+                                 int32_t head_dim, int32_t max_num_chunks, void* out, float* lse,
+                                 void* stream) {
+    sa_status_t s;
+    if ((s = check_dtype(out_dtype)) != SA_OK) return s;
+    if (!part_m || !part_d || !part_acc || !out)
+        return fail(SA_EINVAL, "sink_attn_merge_rows: null pointer argument");
+    if (num_rows < 0) return fail(SA_EINVAL, "num_rows must be >= 0, got %d", num_rows);
+    if (num_q_heads < 1) return fail(SA_EINVAL, "num_q_heads must be >= 1");
+    if (head_dim != 64) return fail(SA_EUNSUPPORTED, "head_dim %d is not supported (only 64)", head_dim);
+    if (max_num_chunks < 1) return fail(SA_EINVAL, "max_num_chunks must be >= 1");
+    if ((int64_t)num_rows * num_q_heads > 0x7fffffffLL)
+        return fail(SA_EINVAL, "num_rows * num_q_heads exceeds the grid limit");
+    if (num_rows == 0) return ok();
+    if ((s = check_device()) != SA_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = sa::launch_merge(out_dtype == SA_BF16, part_m, part_d, part_acc, nullptr, 1,
+                                    max_num_chunks, num_rows, num_q_heads, out, lse, st);
+    return finish_launch(e, st, "sink_attn_merge_rows");
+}
+
 }  // extern "C"
 
 namespace {

@@ -32,8 +32,14 @@ __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) { return f32_to_bf16_bits(x); }
 
-// grid.x: block of query rows (prefill) or key chunk (split); grid.y: KV head; grid.z: sequence.
-template <typename T, bool kSplit>
+// What a launch computes: the whole attention of blocks of query rows (kRows),
+// the chunk states of single-query sequences (kDecodeSplit), or the chunk states
+// of blocks of query rows (kRowsSplit: one key chunk per launch index).
+enum Mode { kRows, kDecodeSplit, kRowsSplit };
+
+// grid.x: block of query rows (kRows, kRowsSplit) or key chunk (kDecodeSplit);
+// grid.y: KV head; grid.z: sequence (kRowsSplit: sequence * max_chunks + chunk).
+template <typename T, Mode kMode>
 __global__ __launch_bounds__(64) void rows_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ sinks, const int32_t* __restrict__ cu_q,
@@ -46,7 +52,9 @@ __global__ __launch_bounds__(64) void rows_kernel(
     const int group = hq / hkv;
     const int rows_per_wave = 64 / group;
     const int lane = threadIdx.x;
-    const int g = blockIdx.y, b = blockIdx.z;
+    constexpr bool kSplit = kMode != kRows;
+    const int g = blockIdx.y;
+    const int b = (kMode == kRowsSplit) ? blockIdx.z / max_chunks : blockIdx.z;
     const int r_local = lane / group, hh = lane % group;
     const int h = g * group + hh;
 
@@ -54,7 +62,7 @@ __global__ __launch_bounds__(64) void rows_kernel(
     const int lk = cu_k[b + 1] - k0;
     int lq, row, key_lo, key_hi;
     bool first_block;
-    if (kSplit) {
+    if (kMode == kDecodeSplit) {
         lq = 1;
         row = r_local;  // one query per sequence: only lanes with r_local == 0 are active
         const int c = blockIdx.x;
@@ -69,24 +77,31 @@ __global__ __launch_bounds__(64) void rows_kernel(
         const int r0 = blockIdx.x * rows_per_wave;
         if (r0 >= lq) return;
         row = r0 + r_local;
-        key_lo = 0;
         const int last = min(r0 + rows_per_wave, lq) - 1;
+        key_lo = 0;
         key_hi = causal ? max(0, min(lk, lk - lq + last + 1)) : lk;
         first_block = true;
+        if (kMode == kRowsSplit) {  // this launch index's chunk of the keys
+            const int c = blockIdx.z % max_chunks;
+            key_lo = c * chunk;
+            key_hi = min(key_hi, key_lo + chunk);
+            first_block = (c == 0);
+        }
     }
     const bool active = (r_local < rows_per_wave) && (row < lq);
     // last key (exclusive) this row may see
-    const int row_limit = (!kSplit && causal) ? min(lk, lk - lq + row + 1) : key_hi;
+    const int row_limit = (kMode != kDecodeSplit && causal) ? min(key_hi, lk - lq + row + 1) : key_hi;
 
     float qr[kD];
     {
-        const int64_t qrow = kSplit ? (int64_t)b : (int64_t)(cu_q[b] + min(row, lq - 1));
+        const int64_t qrow = (kMode == kDecodeSplit) ? (int64_t)b : (int64_t)(cu_q[b] + min(row, lq - 1));
         const T* qp = q + (qrow * hq + (active ? h : g * group)) * kD;
 #pragma unroll
         for (int d = 0; d < kD; ++d) qr[d] = to_f32<T>(qp[d]) * scale_log2;
     }
     float m = (first_block && active) ? sinks[h] * kLog2e : kNegInf;
-    float dsum = 1.0f;
+    // the scale starts at 1 with the sink; an empty chunk state has scale 0
+    float dsum = (first_block || kMode == kDecodeSplit) ? 1.0f : 0.0f;
     float acc[kD];
 #pragma unroll
     for (int d = 0; d < kD; ++d) acc[d] = 0.0f;
@@ -132,8 +147,9 @@ __global__ __launch_bounds__(64) void rows_kernel(
     if (!active) return;
 
     if (kSplit) {
-        const int c = blockIdx.x;
-        const int64_t slot = ((int64_t)b * hq + h) * max_chunks + c;
+        const int c = (kMode == kDecodeSplit) ? blockIdx.x : blockIdx.z % max_chunks;
+        const int64_t srow = (kMode == kDecodeSplit) ? (int64_t)b : (int64_t)cu_q[b] + row;
+        const int64_t slot = (srow * hq + h) * max_chunks + c;
         part_m[slot] = (m == kNegInf) ? kNegInf : m * kLn2;
         part_d[slot] = dsum;
         float* pa = part_acc + slot * kD;
@@ -166,12 +182,12 @@ hipError_t launch_generic_prefill(bool bf16, const void* q, const void* k, const
     dim3 grid(ceil_div(max_lq, rows_per_wave), hkv, batch);
     const float sl = sm_scale * kLog2e;
     if (bf16)
-        hipLaunchKernelGGL((rows_kernel<uint16_t, false>), grid, dim3(64), 0, stream,
+        hipLaunchKernelGGL((rows_kernel<uint16_t, kRows>), grid, dim3(64), 0, stream,
                            (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, sinks, cu_q,
                            cu_k, hq, hkv, sl, causal, 0, 0, (uint16_t*)out, lse, nullptr, nullptr,
                            nullptr);
     else
-        hipLaunchKernelGGL((rows_kernel<float, false>), grid, dim3(64), 0, stream, (const float*)q,
+        hipLaunchKernelGGL((rows_kernel<float, kRows>), grid, dim3(64), 0, stream, (const float*)q,
                            (const float*)k, (const float*)v, sinks, cu_q, cu_k, hq, hkv, sl, causal,
                            0, 0, (float*)out, lse, nullptr, nullptr, nullptr);
     return hipGetLastError();
@@ -185,14 +201,37 @@ hipError_t launch_generic_decode_split(bool bf16, const void* q, const void* k, 
     dim3 grid(max_chunks, hkv, batch);
     const float sl = sm_scale * kLog2e;
     if (bf16)
-        hipLaunchKernelGGL((rows_kernel<uint16_t, true>), grid, dim3(64), 0, stream,
+        hipLaunchKernelGGL((rows_kernel<uint16_t, kDecodeSplit>), grid, dim3(64), 0, stream,
                            (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, sinks,
                            nullptr, cu_k, hq, hkv, sl, 0, chunk, max_chunks, nullptr, nullptr,
                            part_m, part_d, part_acc);
     else
-        hipLaunchKernelGGL((rows_kernel<float, true>), grid, dim3(64), 0, stream, (const float*)q,
+        hipLaunchKernelGGL((rows_kernel<float, kDecodeSplit>), grid, dim3(64), 0, stream, (const float*)q,
                            (const float*)k, (const float*)v, sinks, nullptr, cu_k, hq, hkv, sl, 0,
                            chunk, max_chunks, nullptr, nullptr, part_m, part_d, part_acc);
+    return hipGetLastError();
+}
+
+hipError_t launch_generic_prefill_split(bool bf16, const void* q, const void* k, const void* v,
+                                        const float* sinks, const int32_t* cu_q,
+                                        const int32_t* cu_k, int batch, int hq, int hkv,
+                                        int max_lq, int chunk, int max_chunks, float sm_scale,
+                                        int causal, float* part_m, float* part_d,
+                                        float* part_acc, hipStream_t stream) {
+    const int group = hq / hkv;
+    const int rows_per_wave = 64 / group;
+    dim3 grid(ceil_div(max_lq, rows_per_wave), hkv, batch * max_chunks);
+    const float sl = sm_scale * kLog2e;
+    if (bf16)
+        hipLaunchKernelGGL((rows_kernel<uint16_t, kRowsSplit>), grid, dim3(64), 0, stream,
+                           (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, sinks, cu_q,
+                           cu_k, hq, hkv, sl, causal, chunk, max_chunks, nullptr, nullptr, part_m,
+                           part_d, part_acc);
+    else
+        hipLaunchKernelGGL((rows_kernel<float, kRowsSplit>), grid, dim3(64), 0, stream,
+                           (const float*)q, (const float*)k, (const float*)v, sinks, cu_q, cu_k, hq,
+                           hkv, sl, causal, chunk, max_chunks, nullptr, nullptr, part_m, part_d,
+                           part_acc);
     return hipGetLastError();
 }
 

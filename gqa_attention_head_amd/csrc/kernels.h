@@ -11,6 +11,12 @@ hipError_t launch_generic_prefill(bool bf16, const void* q, const void* k, const
                                   const float* sinks, const int32_t* cu_q, const int32_t* cu_k,
                                   int batch, int hq, int hkv, int max_lq, float sm_scale,
                                   int causal, void* out, float* lse, hipStream_t stream);
+hipError_t launch_generic_prefill_split(bool bf16, const void* q, const void* k, const void* v,
+                                        const float* sinks, const int32_t* cu_q,
+                                        const int32_t* cu_k, int batch, int hq, int hkv,
+                                        int max_lq, int chunk, int max_chunks, float sm_scale,
+                                        int causal, float* part_m, float* part_d,
+                                        float* part_acc, hipStream_t stream);
 hipError_t launch_generic_decode_split(bool bf16, const void* q, const void* k, const void* v,
                                        const float* sinks, const int32_t* cu_k, int batch, int hq,
                                        int hkv, int chunk, int max_chunks, float sm_scale,
@@ -25,12 +31,20 @@ hipError_t launch_mfma_decode_split(const void* q, const void* k, const void* v,
                                     float* part_m, float* part_d, float* part_acc,
                                     hipStream_t stream);
 bool mfma_prefill_supported(int group);
+// Chunk states of every (query row, head, key chunk) instead of the output.
+hipError_t launch_mfma_prefill_split(const void* q, const void* k, const void* v,
+                                     const float* sinks, const int32_t* cu_q, const int32_t* cu_k,
+                                     int batch, int hq, int hkv, int max_lq, int chunk,
+                                     int max_chunks, float sm_scale, int causal, void* out,
+                                     float* lse, float* part_m, float* part_d, float* part_acc,
+                                     hipStream_t stream);
 hipError_t launch_mfma_prefill(const void* q, const void* k, const void* v, const float* sinks,
                                const int32_t* cu_q, const int32_t* cu_k, int batch, int hq,
                                int hkv, int max_lq, float sm_scale, int causal, void* out,
                                float* lse, hipStream_t stream);
 
-// Log-sum-exp combination of split-KV chunk states.
+// Log-sum-exp combination of split-KV chunk states.  cu_k == nullptr: every
+// one of the max_chunks slots of each of the `batch` rows is combined.
 hipError_t launch_merge(bool out_bf16, const float* part_m, const float* part_d,
                         const float* part_acc, const int32_t* cu_k, int chunk, int max_chunks,
                         int batch, int hq, void* out, float* lse, hipStream_t stream);

@@ -47,7 +47,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void merge_kernel(
 
     // The first group's loads do not wait for the sequence length: they read
     // slots clamped to the buffer's last one and are masked once nch is known.
-    const int k_lo = cu_k[b], k_hi = cu_k[b + 1];
+    const int k_lo = (cu_k != nullptr) ? cu_k[b] : 0;
+    const int k_hi = (cu_k != nullptr) ? cu_k[b + 1] : 0;
     float m_ld, d_ld, av[kGroup];
     auto load_group = [&](int c0) {
         // lane u < kGroup: chunk c0 + u's m and d; every lane: its dimension of
@@ -61,7 +62,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void merge_kernel(
     };
     load_group(0);
     __builtin_amdgcn_sched_barrier(0);
-    const int nch = min(max_chunks, max(1, ceil_div(k_hi - k_lo, chunk)));
+    // without sequence lengths every slot holds a state (rows of a split prefill)
+    const int nch = (cu_k != nullptr) ? min(max_chunks, max(1, ceil_div(k_hi - k_lo, chunk)))
+                                      : max_chunks;
 
     float big = kNegInf, acc = 0.0f, den = 0.0f;
     for (int c0 = 0;;) {

@@ -42,13 +42,20 @@ constexpr int kSegs = kBK * kD / 8; // 16-byte segments per K (or V) tile
 // below 2^kRescaleThreshold and the rescale multiply is skipped for the tile.
 constexpr float kRescaleThreshold = 8.0f;
 
-template <int G>
+// kSplit: the keys of each sequence are cut into chunks of `chunk` keys, one
+// chunk per launch index (the slowest grid dimension), and the kernel writes each
+// row's state after its chunk (m in natural-log units, d, unnormalised acc) to
+// slot (row, head, chunk) instead of the normalised output.  The sink enters
+// chunk 0's state only; a chunk a row cannot see leaves (m = -inf, d = 0, acc = 0).
+template <int G, bool kSplit>
 __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4)))
 void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                   const uint16_t* __restrict__ v, const float* __restrict__ sinks,
                   const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int hq,
                   int hkv, int batch, int n_qblocks, float scale_log2, int causal,
-                  uint16_t* __restrict__ out, float* __restrict__ lse) {
+                  uint16_t* __restrict__ out, float* __restrict__ lse, int chunk, int max_chunks,
+                  float* __restrict__ part_m, float* __restrict__ part_d,
+                  float* __restrict__ part_acc) {
     constexpr int kThreads = 64 * G;
     constexpr int kPer = (kSegs + kThreads - 1) / kThreads;
     __shared__ uint16_t kl[2][kBK * kStride];
@@ -60,7 +67,9 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     // to XCDs round-robin), each XCD keeps its own pairs, so a K/V head is
     // cached in one XCD's L2 only.
     const int pairs = batch * hkv;
-    const int bid = blockIdx.x;
+    const int per_chunk = pairs * n_qblocks;
+    const int c = kSplit ? (int)(blockIdx.x / per_chunk) : 0;
+    const int bid = kSplit ? (int)(blockIdx.x % per_chunk) : (int)blockIdx.x;
     int pair, qb;
     if (pairs % 8 == 0) {
         const int xcd = bid % 8, j = bid / 8, per_xcd = pairs / 8;
@@ -83,9 +92,15 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     const bool row_ok = row < lq;
     const int last = min(r0 + kBQ, lq) - 1;
     // keys [0, kend) are visible to some row of the block; [0, full_end) to every row.
-    const int kend = causal ? max(0, min(lk, lk - lq + last + 1)) : lk;
-    const int full_end = causal ? max(0, min(lk, lk - lq + r0 + 1)) : lk;
-    const int row_lim = causal ? min(lk, lk - lq + row + 1) : lk;
+    int kend = causal ? max(0, min(lk, lk - lq + last + 1)) : lk;
+    int full_end = causal ? max(0, min(lk, lk - lq + r0 + 1)) : lk;
+    // this launch's keys start at k_lo (0 unless split); rows see keys below row_lim
+    const int k_lo = c * chunk;
+    if (kSplit) {
+        kend = min(kend, k_lo + chunk);
+        full_end = min(full_end, k_lo + chunk);
+    }
+    const int row_lim = min(kend, causal ? lk - lq + row + 1 : lk);
 
     // B operand of S^T = K Q^T: lane holds Q[row][16*ks + 8*half .. +7].
     bf16x8 qop[4];
@@ -97,8 +112,8 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 
     // Running state (base 2): the maximum starts at the sink (the first and only
     // block of keys holds it) and the scale at 1, split over the two lane halves.
-    float m = sinks[h] * kLog2e;
-    float dl = (half == 0) ? 1.0f : 0.0f;
+    float m = (c == 0) ? sinks[h] * kLog2e : kNegInf;
+    float dl = (half == 0 && c == 0) ? 1.0f : 0.0f;
     f32x16 o[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -132,14 +147,16 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
         }
     };
 
-    const int ntiles = ceil_div(kend, kBK);
-    if (ntiles > 0) {
-        gload(0);
-        lstore(0);
+    // 64-key tiles t_first .. ntiles - 1 cover [k_lo, kend)
+    const int t_first = k_lo / kBK;
+    const int ntiles = (kend > k_lo) ? ceil_div(kend, kBK) : t_first;
+    if (ntiles > t_first) {
+        gload(t_first * kBK);
+        lstore(t_first & 1);
     }
     __syncthreads();
     const int g4 = lane / 16, c16 = lane % 16;
-    for (int t = 0; t < ntiles; ++t) {
+    for (int t = t_first; t < ntiles; ++t) {
         const int j0 = t * kBK;
         const int buf = t & 1;
         const bool more = t + 1 < ntiles;
@@ -159,13 +176,13 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
                 s[kb] = mfma32x32x16(a, qop[ks], s[kb]);
             }
         }
-        if (j0 + kBK > full_end) {  // diagonal or ragged tile (uniform)
+        if (j0 + kBK > full_end || j0 < k_lo) {  // diagonal, ragged or chunk-edge tile (uniform)
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = j0 + 32 * kb + 8 * (i / 4) + 4 * half + (i % 4);
-                    if (key >= row_lim) s[kb][i] = kNegInf;
+                    if (key >= row_lim || key < k_lo) s[kb][i] = kNegInf;
                 }
         }
         // row max of the tile (sm_scale > 0, so the max of raw scores scales)
@@ -222,6 +239,22 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     const float dsum = sum_xor32(dl);
     if (!row_ok) return;
     const int64_t orow = (int64_t)(q0 + row) * hq + h;
+    if (kSplit) {
+        const int64_t slot = orow * max_chunks + c;
+        float* pa = part_acc + slot * kD;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                // o[mt][4j + e] = O^T[dim 32*mt + 8*j + 4*half + e][row]
+                *reinterpret_cast<f32x4*>(pa + 32 * mt + 8 * j + 4 * half) =
+                    f32x4{o[mt][4 * j], o[mt][4 * j + 1], o[mt][4 * j + 2], o[mt][4 * j + 3]};
+        if (half == 0) {
+            part_m[slot] = (m == kNegInf) ? kNegInf : m * kLn2;
+            part_d[slot] = dsum;
+        }
+        return;
+    }
     const bool empty = (m == kNegInf) || !(dsum > 0.0f);
     const float inv = empty ? 0.0f : 1.0f / dsum;
     uint16_t* op = out + orow * kD;
@@ -244,14 +277,22 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 template <int G>
 hipError_t launch_g(const void* q, const void* k, const void* v, const float* sinks,
                     const int32_t* cu_q, const int32_t* cu_k, int batch, int hq, int hkv,
-                    int max_lq, float sm_scale, int causal, void* out, float* lse,
+                    int max_lq, float sm_scale, int causal, void* out, float* lse, int chunk,
+                    int max_chunks, float* part_m, float* part_d, float* part_acc,
                     hipStream_t stream) {
     const int n_qblocks = ceil_div(max_lq, kBQ);
-    const int64_t blocks = (int64_t)batch * hkv * n_qblocks;
-    hipLaunchKernelGGL((prefill_mfma<G>), dim3((unsigned)blocks), dim3(64 * G), 0, stream,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, sinks, cu_q,
-                       cu_k, hq, hkv, batch, n_qblocks, sm_scale * kLog2e, causal, (uint16_t*)out,
-                       lse);
+    const bool split = part_m != nullptr;
+    const int64_t blocks = (int64_t)batch * hkv * n_qblocks * (split ? max_chunks : 1);
+    if (split)
+        hipLaunchKernelGGL((prefill_mfma<G, true>), dim3((unsigned)blocks), dim3(64 * G), 0,
+                           stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                           sinks, cu_q, cu_k, hq, hkv, batch, n_qblocks, sm_scale * kLog2e, causal,
+                           nullptr, nullptr, chunk, max_chunks, part_m, part_d, part_acc);
+    else
+        hipLaunchKernelGGL((prefill_mfma<G, false>), dim3((unsigned)blocks), dim3(64 * G), 0,
+                           stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                           sinks, cu_q, cu_k, hq, hkv, batch, n_qblocks, sm_scale * kLog2e, causal,
+                           (uint16_t*)out, lse, 0, 1, nullptr, nullptr, nullptr);
     return hipGetLastError();
 }
 
@@ -265,12 +306,22 @@ hipError_t launch_mfma_prefill(const void* q, const void* k, const void* v, cons
                                const int32_t* cu_q, const int32_t* cu_k, int batch, int hq,
                                int hkv, int max_lq, float sm_scale, int causal, void* out,
                                float* lse, hipStream_t stream) {
+    return launch_mfma_prefill_split(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, 0, 1,
+                                     sm_scale, causal, out, lse, nullptr, nullptr, nullptr, stream);
+}
+
+hipError_t launch_mfma_prefill_split(const void* q, const void* k, const void* v,
+                                     const float* sinks, const int32_t* cu_q, const int32_t* cu_k,
+                                     int batch, int hq, int hkv, int max_lq, int chunk,
+                                     int max_chunks, float sm_scale, int causal, void* out,
+                                     float* lse, float* part_m, float* part_d, float* part_acc,
+                                     hipStream_t stream) {
     switch (hq / hkv) {
-        case 1: return launch_g<1>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, stream);
-        case 2: return launch_g<2>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, stream);
-        case 4: return launch_g<4>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, stream);
-        case 8: return launch_g<8>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, stream);
-        case 16: return launch_g<16>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, stream);
+        case 1: return launch_g<1>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, chunk, max_chunks, part_m, part_d, part_acc, stream);
+        case 2: return launch_g<2>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, chunk, max_chunks, part_m, part_d, part_acc, stream);
+        case 4: return launch_g<4>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, chunk, max_chunks, part_m, part_d, part_acc, stream);
+        case 8: return launch_g<8>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, chunk, max_chunks, part_m, part_d, part_acc, stream);
+        case 16: return launch_g<16>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, chunk, max_chunks, part_m, part_d, part_acc, stream);
         default: return hipErrorInvalidValue;
     }
 }

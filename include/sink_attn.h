@@ -150,6 +150,51 @@ sa_status_t sink_attn_decode(sa_dtype_t dtype, const void *q, const void *k, con
                              float sm_scale, float *part_m, float *part_d, float *part_acc,
                              void *out, float *lse, void *stream);
 
+/*
+ * Split-KV prefill, first pass: the prefill problem of sink_attn_prefill with the
+ * keys of every sequence cut into chunks of kv_chunk_size keys, chunk c covering
+ * keys [c*C, min((c+1)*C, L_k)) -- the split along the KV length of "GPT-OSS on
+ * day 0" (Perplexity), Kernels for GPT-OSS / Sink attention, with the sink in the
+ * first block only.  For every query row r (absolute row in q), query head h and
+ * chunk c < max_num_chunks it writes the state (m, d, acc) after the keys of
+ * chunk c that row r may see (the whole chunk, or its causal part); the sink is
+ * part of chunk 0's state only.  A chunk the row cannot see (and every slot
+ * c >= ceil(L_k / C)) holds the empty state m = -inf, d = 0, acc = 0, except
+ * that chunk 0 always carries the sink (m = sink, d = 1, acc = 0 when no key is
+ * visible).  m is in natural-log units, acc is unnormalised.
+ *
+ *   Arguments as for sink_attn_prefill, plus kv_chunk_size >= 1 and
+ *   max_num_chunks >= ceil(max_seqlen_k / kv_chunk_size) (>= 1).
+ *   part_m, part_d  [total_q, Hq, max_num_chunks] float32 (caller-owned)
+ *   part_acc        [total_q, Hq, max_num_chunks, D] float32 (caller-owned)
+ * Errors as for sink_attn_prefill; SA_EINVAL for a too small max_num_chunks or a
+ * launch grid beyond the device limits.
+ */
+sa_status_t sink_attn_prefill_split(sa_dtype_t dtype, const void *q, const void *k, const void *v,
+                                    const float *sinks, const int32_t *cu_seqlens_q,
+                                    const int32_t *cu_seqlens_k, int32_t batch,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                    int32_t kv_chunk_size, int32_t max_num_chunks, float sm_scale,
+                                    int32_t causal, float *part_m, float *part_d, float *part_acc,
+                                    void *stream);
+
+/*
+ * Log-sum-exp combination of every slot of per-row chunk states, as written by
+ * sink_attn_prefill_split (the same combination as sink_attn_merge: with
+ * M = max_c m_c, out = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) d_c and
+ * lse = M + ln sum_c e^(m_c - M) d_c; all m_c = -inf gives out = 0, lse = -inf).
+ *
+ *   part_m, part_d  [num_rows, Hq, max_num_chunks] float32;  part_acc [.., D]
+ *   out             [num_rows, Hq, D] out_dtype;  lse nullable [num_rows, Hq] float32
+ * Errors: SA_EINVAL for null pointers, num_rows < 0, Hq < 1, max_num_chunks < 1;
+ * SA_EUNSUPPORTED for head_dim != 64.  num_rows = 0 does nothing.
+ */
+sa_status_t sink_attn_merge_rows(sa_dtype_t out_dtype, const float *part_m, const float *part_d,
+                                 const float *part_acc, int32_t num_rows, int32_t num_q_heads,
+                                 int32_t head_dim, int32_t max_num_chunks, void *out, float *lse,
+                                 void *stream);
+
 /* Text of the calling thread's last non-OK status ("" if none).  Valid until the next call. */
 const char *sink_attn_last_error(void);
 

@@ -80,6 +80,21 @@ def _decode(lib, **kw):
     return lib.sink_attn_decode(*a.values())
 
 
+def _prefill_split(lib, **kw):
+    a = dict(dtype=sa.SA_BF16, q=P, k=P, v=P, sinks=P, cu_q=P, cu_k=P, batch=2, hq=64, hkv=8,
+             d=64, max_q=4096, max_k=4096, chunk=1024, max_chunks=4, scale=0.125, causal=1,
+             pm=P, pd=P, pa=P, stream=NULL)
+    a.update(kw)
+    return lib.sink_attn_prefill_split(*a.values())
+
+
+def _merge_rows(lib, **kw):
+    a = dict(dtype=sa.SA_BF16, pm=P, pd=P, pa=P, rows=100, hq=64, d=64, max_chunks=4, out=P,
+             lse=NULL, stream=NULL)
+    a.update(kw)
+    return lib.sink_attn_merge_rows(*a.values())
+
+
 def _merge(lib, **kw):
     a = dict(dtype=sa.SA_BF16, pm=P, pd=P, pa=P, cu_k=P, chunk=512, max_chunks=8, batch=2,
              hq=64, d=64, out=P, lse=NULL, stream=NULL)
@@ -179,3 +194,39 @@ def test_product_does_not_touch_the_oracle():
     res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
                          env=dict(os.environ, PYTHONPATH=ROOT), check=True)
     assert res.stdout.strip() == "False"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pm=NULL), sa.SA_EINVAL),
+    (dict(cu_q=NULL), sa.SA_EINVAL),
+    (dict(chunk=0), sa.SA_EINVAL),
+    (dict(max_chunks=3), sa.SA_EINVAL),        # ceil(4096 / 1024) = 4 slots needed
+    (dict(causal=3), sa.SA_EINVAL),
+    (dict(hq=64, hkv=6), sa.SA_EINVAL),
+    (dict(d=80), sa.SA_EUNSUPPORTED),
+    (dict(scale=0.0), sa.SA_EINVAL),
+    (dict(dtype=sa.SA_FP32, batch=3000, max_chunks=40, max_k=40960), sa.SA_EINVAL),  # generic grid
+])
+def test_prefill_split_rejects(lib, kw, status):
+    assert _prefill_split(lib, **kw) == status
+    assert lib.sink_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pa=NULL), sa.SA_EINVAL),
+    (dict(out=NULL), sa.SA_EINVAL),
+    (dict(rows=-1), sa.SA_EINVAL),
+    (dict(hq=0), sa.SA_EINVAL),
+    (dict(max_chunks=0), sa.SA_EINVAL),
+    (dict(d=128), sa.SA_EUNSUPPORTED),
+    (dict(dtype=5), sa.SA_EINVAL),
+])
+def test_merge_rows_rejects(lib, kw, status):
+    assert _merge_rows(lib, **kw) == status
+    assert lib.sink_attn_last_error().decode()
+
+
+def test_split_entry_points_empty_work_needs_no_device(lib):
+    """Zero query rows / zero merge rows are valid no-ops (no device touched)."""
+    assert _prefill_split(lib, max_q=0) == sa.SA_OK
+    assert _merge_rows(lib, rows=0) == sa.SA_OK

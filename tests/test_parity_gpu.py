@@ -304,3 +304,110 @@ def test_decode_graph_replays(orc):
         out, lse = g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager2[0]) and torch.equal(lse, eager2[1]), f"replay {i} (new q)"
+
+
+# ---------------------------------------------------------------- split-KV prefill
+
+def run_prefill_split(dev: "H.Device", chunk: int, causal=None):
+    wl = dev.wl
+    causal = wl.causal if causal is None else causal
+    nch = max(1, -(-dev.max_lk // chunk))
+    pm, pd, pa = sa.prefill_split(dev.q, dev.k, dev.v, dev.sinks, dev.cu_q, dev.cu_k,
+                                  dev.max_lq, dev.max_lk, chunk, wl.sm_scale, causal=causal,
+                                  max_num_chunks=nch)
+    out, lse = sa.merge_rows(pm, pd, pa, out_dtype=dev.dtype, return_lse=True)
+    torch.cuda.synchronize()
+    return pm, pd, pa, out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("group", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("chunk", [64, 100, 1024])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_split_cases(orc, group, chunk, causal):
+    """Split-KV prefill + row merge against the plain definition: several tiles per
+    chunk, ragged chunk ends, chunks not aligned to the 64-key tiles, L_q < L_k."""
+    wl = W.random_case(110 + group, batch=3, hq=2 * group, hkv=2, max_q=150, max_k=900,
+                       causal=causal, sink_values=([-np.inf, 20.0, -20.0, 0.5] * group)[:2 * group])
+    dev = H.Device(wl)
+    _, _, _, out, lse = run_prefill_split(dev, chunk)
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    H.assert_close(out, ref, bf16=True)
+    H.assert_lse_close(lse, ref_lse, bf16=True)
+
+
+@pytest.mark.parametrize("chunk", [64, 96])
+def test_prefill_split_fp32(orc, chunk):
+    wl = W.random_case(131, dtype="fp32", batch=2, hq=8, hkv=2, max_q=100, max_k=400)
+    dev = H.Device(wl)
+    _, _, _, out, lse = run_prefill_split(dev, chunk)
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    H.assert_close(out, ref, bf16=False)
+    H.assert_lse_close(lse, ref_lse, bf16=False)
+
+
+@pytest.mark.parametrize("group", [8, 3])
+def test_prefill_split_chunk_states(orc, group):
+    """Each chunk state against the definition restricted to the chunk: the keys of
+    chunk c the row may see, with the sink in chunk 0 only; chunks a row cannot see
+    hold (m = -inf, d = 0, acc = 0)."""
+    chunk = 128
+    wl = W.random_case(140 + group, batch=2, hq=2 * group, hkv=2, max_q=200, max_k=700,
+                       sink_values=([-np.inf, 1.5, -20.0, 0.5] * group)[:2 * group])
+    dev = H.Device(wl)
+    pm, pd, pa, _, _ = run_prefill_split(dev, chunk)
+    pm, pd, pa = (t.cpu().numpy().astype(np.float64) for t in (pm, pd, pa))
+    nch = pm.shape[2]
+    rng = np.random.default_rng(5)
+    rows = rng.choice(int(wl.cu_q[-1]), 12, replace=False)
+    for r in rows:
+        b = int(np.searchsorted(wl.cu_q, r, side="right") - 1)
+        i = int(r - wl.cu_q[b])
+        lq, lk = int(wl.seqlens_q[b]), int(wl.seqlens_k[b])
+        vis = lk - lq + i + 1 if wl.causal else lk
+        for c in range(nch):
+            lo, hi = c * chunk, min((c + 1) * chunk, max(vis, 0))
+            n = max(0, hi - lo)
+            kk = wl.k32[wl.cu_k[b] + lo:wl.cu_k[b] + lo + n]
+            vv = wl.v32[wl.cu_k[b] + lo:wl.cu_k[b] + lo + n]
+            sinks = wl.sinks if c == 0 else np.full_like(wl.sinks, -np.inf)
+            ref, ref_lse = orc.attention(wl.q32[r:r + 1], kk, vv, sinks, np.array([0, 1]),
+                                         np.array([0, n]), wl.sm_scale, causal=False,
+                                         nthreads=1)
+            for h in range(wl.num_q_heads):
+                m, d = pm[r, h, c], pd[r, h, c]
+                if not np.isfinite(ref_lse[0, h]):
+                    assert m == -np.inf and np.all(pa[r, h, c] == 0.0), (r, h, c)
+                    if c > 0:
+                        assert d == 0.0, (r, h, c)
+                    continue
+                got_lse = m + np.log(d)
+                assert abs(got_lse - ref_lse[0, h]) <= H.BF16_LSE, (r, h, c, got_lse, ref_lse[0, h])
+                assert np.abs(pa[r, h, c] / d - ref[0, h]).max() <= H.BF16_MAX_ABS, (r, h, c)
+
+
+def test_prefill_split_mixed_varlen(orc):
+    """Workload 5 (prefill chunks over cached keys and single-token decodes, sinks from
+    {-inf, -20, 0, +20, N(0,1)}) through the split prefill with 1024-key chunks."""
+    wl = W.workload(5)
+    dev = H.Device(wl)
+    _, _, _, out, lse = run_prefill_split(dev, 1024)
+    rng = np.random.default_rng(7)
+    rows = np.sort(rng.choice(int(wl.cu_q[-1]), 256, replace=False))
+    ref, ref_lse = orc.workload(wl, rows=rows, nthreads=NTHREADS)
+    H.assert_close(out[rows], ref, bf16=True)
+    H.assert_lse_close(lse[rows], ref_lse, bf16=True)
+
+
+def test_prefill_split_matches_unsplit():
+    """The split and unsplit prefill agree on the 4 x 4096 causal workload (sampled
+    rows), within the bf16 tolerance (split-invariance of the method)."""
+    wl = W.workload(3)
+    dev = H.Device(wl)
+    _, _, _, out, lse = run_prefill_split(dev, 1024)
+    full, full_lse = sa.prefill(dev.q, dev.k, dev.v, dev.sinks, dev.cu_q, dev.cu_k, dev.max_lq,
+                                dev.max_lk, wl.sm_scale, causal=True, return_lse=True)
+    torch.cuda.synchronize()
+    full = full.float().cpu().numpy().astype(np.float64)
+    full_lse = full_lse.cpu().numpy().astype(np.float64)
+    assert np.abs(out - full).max() <= H.BF16_MAX_ABS
+    assert np.abs(lse - full_lse).max() <= 1e-4

@@ -153,6 +153,58 @@ def bench_prefill(steps: int, warmup: int):
                 tflops=flops / (mean_ms * 1e-3) / 1e12, wl=wl)
 
 
+LONG_KV = dict(lq=256, lk=131072, chunk=16384)  # chunked prefill over a long cache
+
+
+def bench_prefill_long_kv(steps: int, warmup: int):
+    """A chunked prefill (256 new tokens over 131072 cached keys, 64/8 heads, bf16):
+    the unsplit kernel (64 workgroups) against the split-KV pass + row merge."""
+    import torch
+    import gqa_attention_head_amd as sa
+    from gqa_attention_head_amd import workloads as W
+
+    lq, lk, chunk = LONG_KV["lq"], LONG_KV["lk"], LONG_KV["chunk"]
+    wl = W.make_workload(f"chunked_prefill_bf16_q{lq}_kv{lk}_h64g8_d64", dtype="bf16",
+                         kind="prefill", seqlens_q=[lq], seqlens_k=[lk], num_q_heads=64,
+                         num_kv_heads=8, head_dim=64, seed=11, causal=True)
+    dev = torch.device("cuda", 0)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, k, v = up(wl.q16), up(wl.k16), up(wl.v16)
+    sinks = torch.from_numpy(wl.sinks).to(dev)
+    cu_q = torch.from_numpy(wl.cu_q).to(dev)
+    cu_k = torch.from_numpy(wl.cu_k).to(dev)
+    nch = -(-lk // chunk)
+    parts = sa.partial_buffers(lq, 64, nch, 64, dev)
+    out = torch.empty_like(q)
+
+    def unsplit():
+        sa.prefill(q, k, v, sinks, cu_q, cu_k, lq, lk, wl.sm_scale, causal=True, out=out)
+
+    def split():
+        sa.prefill_split(q, k, v, sinks, cu_q, cu_k, lq, lk, chunk, wl.sm_scale,
+                         max_num_chunks=nch, partials=parts)
+        sa.merge_rows(*parts, out=out)
+
+    res = {}
+    for name, fn in (("unsplit", unsplit), ("split", split)):
+        for _ in range(warmup):
+            fn()
+        _sync()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        _sync()
+        ms = e0.elapsed_time(e1) / steps
+        res[name] = {"ms": round(ms, 4), "tflops": round(wl.prefill_flops() / (ms * 1e-3) / 1e12, 2)}
+    res["split"]["kv_chunk"] = chunk
+    return dict(workload=wl.name, flops=wl.prefill_flops(), **res)
+
+
 def cpu_baseline(dec_wl, pre_wl, budget_s: float = 20.0):
     """The fp64 oracle, untuned, on the host: decode over whole sequences of the decode
     workload, prefill over sampled query rows of the prefill workload."""
@@ -241,6 +293,7 @@ def main(argv=None):
 
     dec = bench_decode(args.steps, args.warmup)
     pre = None if args.no_prefill else bench_prefill(args.prefill_steps, max(2, args.warmup // 5))
+    long_kv = None if args.no_prefill else bench_prefill_long_kv(args.prefill_steps, 2)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(dec["wl"], pre["wl"] if pre else __import__(
@@ -280,10 +333,12 @@ def main(argv=None):
         line["prefill"] = {
             "workload": pre["workload"], "value": round(pre["tflops"], 2), "unit": "TFLOP/s",
             "ms": round(pre["ms_mean"], 4), "flops": pre["flops"],
-            "roofline": {"kernel": "prefill_mfma<8>", "bound": "mfma",
+            "roofline": {"kernel": "prefill_mfma<8, false>", "bound": "mfma",
                          "achieved": round(pre["tflops"], 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(pre["tflops"] / BF16_PEAK_TFLOPS, 4),
                          "traffic": traffic.get("prefill"), "algorithmic_flops": pre["flops"]}}
+    if long_kv is not None:
+        line["prefill_long_kv"] = long_kv
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

@@ -205,6 +205,41 @@ def bench_prefill_long_kv(steps: int, warmup: int):
     return dict(workload=wl.name, flops=wl.prefill_flops(), **res)
 
 
+ROUTER = dict(tokens=1 << 20, experts=128, k=4, copies=2)
+
+
+def bench_router(steps: int, warmup: int):
+    """Top-K-then-softmax expert routing over 2^20 tokens x 128 experts, top-4 (bf16
+    logits, two rotated copies of 268 MB so the last-level cache cannot serve repeats)."""
+    import torch
+    import gqa_attention_head_amd as sa
+    from gqa_attention_head_amd import workloads as W
+
+    t, e, k = ROUTER["tokens"], ROUTER["experts"], ROUTER["k"]
+    bits, _ = W.router_logits(12, t, e)
+    dev = torch.device("cuda", 0)
+    lg0 = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    lgs = [lg0] + [lg0.clone() for _ in range(ROUTER["copies"] - 1)]
+    idx = torch.empty(t, k, device=dev, dtype=torch.int32)
+    w = torch.empty(t, k, device=dev, dtype=torch.bfloat16)
+    for i in range(warmup):
+        sa.topk_softmax(lgs[i % len(lgs)], k, indices=idx, weights=w)
+    _sync()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        sa.topk_softmax(lgs[i % len(lgs)], k, indices=idx, weights=w)
+    e1.record()
+    _sync()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = t * e * 2 + t * k * (4 + 2)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"router_topk_softmax_bf16_t{t}_e{e}_k{k}", "ms": round(ms, 5),
+            "roofline": {"kernel": f"topk_softmax_kernel<{e}, {k}>", "bound": "hbm",
+                         "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}}
+
+
 def cpu_baseline(dec_wl, pre_wl, budget_s: float = 20.0):
     """The fp64 oracle, untuned, on the host: decode over whole sequences of the decode
     workload, prefill over sampled query rows of the prefill workload."""
@@ -278,7 +313,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="decode only (skips the prefill, long-KV prefill and router legs)")
     args = ap.parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -294,6 +330,7 @@ def main(argv=None):
     dec = bench_decode(args.steps, args.warmup)
     pre = None if args.no_prefill else bench_prefill(args.prefill_steps, max(2, args.warmup // 5))
     long_kv = None if args.no_prefill else bench_prefill_long_kv(args.prefill_steps, 2)
+    router = None if args.no_prefill else bench_router(50, 5)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(dec["wl"], pre["wl"] if pre else __import__(
@@ -339,6 +376,8 @@ def main(argv=None):
                          "traffic": traffic.get("prefill"), "algorithmic_flops": pre["flops"]}}
     if long_kv is not None:
         line["prefill_long_kv"] = long_kv
+    if router is not None:
+        line["router"] = router
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

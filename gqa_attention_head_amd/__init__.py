@@ -22,7 +22,7 @@ SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_ELAUNCH = 0, 1, 2, 3
 SA_FP32, SA_BF16 = 0, 1
 EXPORTS = ("sink_attn_prefill", "sink_attn_decode_split", "sink_attn_merge",
            "sink_attn_decode", "sink_attn_prefill_split", "sink_attn_merge_rows",
-           "sink_attn_last_error")
+           "sink_attn_last_error", "moe_topk_softmax")
 
 
 class SinkAttnError(RuntimeError):
@@ -66,6 +66,8 @@ def load_library():
                                             i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp]
     lib.sink_attn_merge_rows.restype = ctypes.c_int
     lib.sink_attn_merge_rows.argtypes = [ctypes.c_int, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.moe_topk_softmax.restype = ctypes.c_int
+    lib.moe_topk_softmax.argtypes = [vp, ctypes.c_int64, i32, i32, vp, vp, vp]
     lib.sink_attn_last_error.restype = ctypes.c_char_p
     lib.sink_attn_last_error.argtypes = []
     _lib = lib
@@ -335,3 +337,25 @@ class DecodeGraph:
         """Run the captured decode on the current stream; returns ``(out, lse)``."""
         self.graph.replay()
         return self.out, self.lse
+
+
+def topk_softmax(logits, k, indices=None, weights=None, stream=None):
+    """Top-K-then-softmax expert routing (``moe_topk_softmax``): logits [T, E] bf16 ->
+    (indices int32 [T, k], weights bf16 [T, k]), experts in rank order."""
+    torch = _torch()
+    lib = load_library()
+    _dev(logits, "logits", torch.bfloat16)
+    if logits.dim() != 2:
+        raise ValueError("logits must be [T, E]")
+    t, e = logits.shape
+    if indices is None:
+        indices = torch.empty(t, k, device=logits.device, dtype=torch.int32)
+    if weights is None:
+        weights = torch.empty(t, k, device=logits.device, dtype=torch.bfloat16)
+    _dev(indices, "indices", torch.int32)
+    _dev(weights, "weights", torch.bfloat16)
+    if tuple(indices.shape) != (t, k) or tuple(weights.shape) != (t, k):
+        raise ValueError("indices and weights must be [T, k]")
+    _check(lib.moe_topk_softmax(_ptr(logits), t, e, int(k), _ptr(indices), _ptr(weights),
+                                _stream(stream)))
+    return indices, weights

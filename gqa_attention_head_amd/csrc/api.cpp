@@ -9,6 +9,7 @@
 #include <string>
 
 #include "kernels.h"
+#include "moe_router.h"
 #include "sink_attn.h"
 
 namespace {
@@ -287,6 +288,22 @@ sa_status_t sink_attn_merge(sa_dtype_t out_dtype, const float* part_m, const flo
     hipError_t e = sa::launch_merge(out_dtype == SA_BF16, part_m, part_d, part_acc, cu_seqlens_k,
                                     kv_chunk_size, max_num_chunks, batch, num_q_heads, out, lse, st);
     return finish_launch(e, st, "sink_attn_merge");
+}
+
+sa_status_t moe_topk_softmax(const void* logits, int64_t num_tokens, int32_t num_experts,
+                             int32_t k, int32_t* indices, void* weights, void* stream) {
+    if (num_tokens < 0) return fail(SA_EINVAL, "num_tokens must be >= 0");
+    if (!sa::topk_softmax_supported(num_experts))
+        return fail(SA_EUNSUPPORTED, "num_experts %d is not supported (8, 16, ..., 512)", num_experts);
+    if (k < 1 || k > 8 || k > num_experts)
+        return fail(SA_EINVAL, "k must be in [1, min(8, num_experts)], got %d", k);
+    if (num_tokens == 0) return ok();  // nothing to read or write: pointers may be null
+    if (!logits || !indices || !weights) return fail(SA_EINVAL, "moe_topk_softmax: null pointer argument");
+    sa_status_t s;
+    if ((s = check_device()) != SA_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = sa::launch_topk_softmax(logits, num_tokens, num_experts, k, indices, weights, st);
+    return finish_launch(e, st, "moe_topk_softmax");
 }
 
 }  // extern "C"

@@ -43,6 +43,12 @@ hipError_t launch_mfma_prefill(const void* q, const void* k, const void* v, cons
                                int hkv, int max_lq, float sm_scale, int causal, void* out,
                                float* lse, hipStream_t stream);
 
+// Top-K-then-softmax routing: bf16 logits [T, E], E in {8, ..., 512} (powers of
+// two), 1 <= k <= 8; int32 indices and bf16 weights [T, k].
+bool topk_softmax_supported(int num_experts);
+hipError_t launch_topk_softmax(const void* logits, int64_t num_tokens, int num_experts, int k,
+                               int32_t* indices, void* weights, hipStream_t stream);
+
 // Log-sum-exp combination of split-KV chunk states.  cu_k == nullptr: every
 // one of the max_chunks slots of each of the `batch` rows is combined.
 hipError_t launch_merge(bool out_bf16, const float* part_m, const float* part_d,

@@ -1,0 +1,209 @@
+// Top-K-then-softmax expert routing, bf16 logits (gfx950).
+//
+// "GPT-OSS on day 0" (Perplexity), MoE section: the gpt-oss router takes the
+// softmax over the K selected experts only, and the expert weights are bf16.
+// For every token: the K experts with the largest logits (larger first, equal
+// logits by lower expert index) and the softmax of those K logits, computed in
+// float32 and rounded to bf16.
+//
+// Layout: a token's E logits are spread over E/32 lanes (one lane for E < 32),
+// each reading its 32 (or E) logits as 16-byte loads, so a wave's loads cover a
+// contiguous run of whole token rows.  Each logit becomes one 32-bit key whose unsigned
+// order is the ranking: the high half is the bf16 bit pattern mapped to an
+// order-preserving unsigned code (-0 folded onto +0), the low half is
+// 0xFFFF - expert, so a larger key is a larger logit or, on a tie, a lower
+// expert index.  Each lane sorts its keys in groups of 8 and keeps its K
+// largest (bitonic merges); round r then takes the largest head key across the
+// token's lanes (DPP and lane-swap maxima, no LDS), and the lane that held it
+// moves on to its next key.
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace sa {
+
+namespace {
+
+// value of a key's order code (high half): 0x8000 + m for +m, 0x8000 - m for -m
+__device__ __forceinline__ float code_value(uint32_t code) {
+    const uint32_t bits = (code >= 0x8000u) ? (code - 0x8000u) : ((0x8000u - code) | 0x8000u);
+    return bf16_bits_to_f32(static_cast<uint16_t>(bits));
+}
+
+// Maximum over each aligned group of kLanes lanes, left in every lane of the group:
+// DPP swaps and mirrors inside a 16-lane row, then the cross-row lane swaps.
+template <int kLanes>
+__device__ __forceinline__ uint32_t group_max(uint32_t x) {
+    auto dpp = [](uint32_t v, auto ctrl) {
+        return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, decltype(ctrl)::value, 0xF, 0xF, false);
+    };
+    if (kLanes >= 2) x = max(x, dpp(x, std::integral_constant<int, 0xB1>{}));   // quad_perm 1,0,3,2
+    if (kLanes >= 4) x = max(x, dpp(x, std::integral_constant<int, 0x4E>{}));   // quad_perm 2,3,0,1
+    if (kLanes >= 8) x = max(x, dpp(x, std::integral_constant<int, 0x141>{}));  // row_half_mirror
+    if (kLanes >= 16) x = max(x, dpp(x, std::integral_constant<int, 0x140>{})); // row_mirror
+    if (kLanes >= 32)
+        x = max(x, (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x401F));       // lane ^ 16
+    if (kLanes >= 64) {
+        auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);            // lane ^ 32
+        x = max(r[0], r[1]);
+    }
+    return x;
+}
+
+constexpr int next_pow2(int k) { return k <= 1 ? 1 : (k <= 2 ? 2 : (k <= 4 ? 4 : 8)); }
+
+// Sorts 8 keys in registers, descending (odd-even merge network, 19 exchanges).
+__device__ __forceinline__ void sort8(uint32_t* x) {
+    auto cx = [&](int a, int b) {
+        const uint32_t hi = max(x[a], x[b]), lo = min(x[a], x[b]);
+        x[a] = hi;
+        x[b] = lo;
+    };
+    cx(0, 1); cx(2, 3); cx(4, 5); cx(6, 7);
+    cx(0, 2); cx(1, 3); cx(4, 6); cx(5, 7);
+    cx(1, 2); cx(5, 6);
+    cx(0, 4); cx(1, 5); cx(2, 6); cx(3, 7);
+    cx(2, 4); cx(3, 5);
+    cx(1, 2); cx(3, 4); cx(5, 6);
+}
+
+// top: the KP largest keys seen so far, descending; g: 8 more keys, descending.
+// Afterwards top holds the KP largest of both, descending (the pairwise maxima
+// of top and reversed g form a bitonic sequence, sorted by a bitonic merge).
+template <int KP>
+__device__ __forceinline__ void merge_top(uint32_t* top, const uint32_t* g) {
+#pragma unroll
+    for (int i = 0; i < KP; ++i) top[i] = max(top[i], g[KP - 1 - i]);
+#pragma unroll
+    for (int half = KP / 2; half >= 1; half /= 2)
+#pragma unroll
+        for (int i = 0; i < KP; ++i)
+            if ((i & half) == 0) {
+                const uint32_t hi = max(top[i], top[i + half]), lo = min(top[i], top[i + half]);
+                top[i] = hi;
+                top[i + half] = lo;
+            }
+}
+
+// One token's E logits are spread over kLanes = E / kPer lanes, kPer = min(E, 32)
+// logits (kPer / 8 16-byte loads) per lane; a wave handles 64 / kLanes tokens per
+// step.  Each lane keeps its KP = next_pow2(K) largest keys, then K rounds pick the
+// largest head across the token's lanes.
+template <int E, int K>
+__global__ __launch_bounds__(256) void topk_softmax_kernel(const uint16_t* __restrict__ logits,
+                                                           int64_t num_tokens,
+                                                           int32_t* __restrict__ indices,
+                                                           uint16_t* __restrict__ weights) {
+    constexpr int kPer = E < 32 ? E : 32;
+    constexpr int kLanes = E / kPer;
+    constexpr int kGroups = kPer / 8;
+    constexpr int KP = next_pow2(K);
+    constexpr int kTokensPerWave = 64 / kLanes;
+    const int lane = threadIdx.x % 64;
+    const int sub = lane % kLanes, grp = lane / kLanes;
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / 64;
+    const int64_t waves = (int64_t)gridDim.x * blockDim.x / 64;
+    // uniform over the wave: every lane takes part in the cross-lane maxima
+    for (int64_t t0 = wave * kTokensPerWave; t0 < num_tokens; t0 += waves * kTokensPerWave) {
+        const int64_t t = t0 + grp;
+        const bool ok = t < num_tokens;
+        u32x4 raw[kGroups];
+#pragma unroll
+        for (int q = 0; q < kGroups; ++q) {
+            raw[q] = u32x4{0u, 0u, 0u, 0u};
+            // plain (cached) loads: the 4 loads of a lane hit each 128-byte line of its
+            // token row in turn, so the line must stay in the cache between them
+            if (ok) raw[q] = *reinterpret_cast<const u32x4*>(logits + t * E + kPer * sub + 8 * q);
+        }
+        uint32_t top[KP];
+#pragma unroll
+        for (int q = 0; q < kGroups; ++q) {
+            uint32_t key[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                // bf16 bits in the high half: H.  The key's high half is the order code
+                // (0x8000 + m for +m, 0x8000 - m for -m, so -0 ranks with +0); its low
+                // half is 0xFFFF - expert.
+                const uint32_t h = (j % 2) ? (raw[q][j / 2] & 0xFFFF0000u) : (raw[q][j / 2] << 16);
+                const uint32_t idc = 0xFFFFu - (uint32_t)(kPer * sub + 8 * q + j);
+                key[j] = (h > 0x80000000u) ? (idc - h) : (h | 0x80000000u | idc);
+            }
+            sort8(key);
+            if (q == 0) {
+#pragma unroll
+                for (int i = 0; i < KP; ++i) top[i] = key[i];
+            } else {
+                merge_top<KP>(top, key);
+            }
+        }
+        // round r: the largest head among the token's lanes wins; its lane moves on
+        uint32_t win[K];
+#pragma unroll
+        for (int r = 0; r < K; ++r) {
+            const uint32_t best = group_max<kLanes>(top[0]);
+            win[r] = best;
+            const bool mine = top[0] == best;  // keys are distinct (expert index)
+#pragma unroll
+            for (int j = 0; j < K - 1 - r; ++j) top[j] = mine ? top[j + 1] : top[j];
+            top[K - 1 - r] = mine ? 0u : top[K - 1 - r];
+        }
+        // softmax over the K winners (all lanes of the token hold them)
+        const float z0 = code_value(win[0] >> 16);
+        float e[K], sum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < K; ++r) {
+            e[r] = fast_exp2((code_value(win[r] >> 16) - z0) * kLog2e);
+            sum += e[r];
+        }
+        const float inv = 1.0f / sum;
+        if (ok && sub == 0) {
+#pragma unroll
+            for (int r = 0; r < K; ++r) {
+                indices[t * K + r] = (int32_t)(0xFFFFu - (win[r] & 0xFFFFu));
+                weights[t * K + r] = f32_to_bf16_bits(e[r] * inv);
+            }
+        }
+    }
+}
+
+template <int E>
+hipError_t launch_experts(const void* logits, int64_t num_tokens, int k, int32_t* indices,
+                          void* weights, hipStream_t stream) {
+    constexpr int kLanes = E / (E < 32 ? E : 32);
+    constexpr int kTokensPerBlock = 4 * (64 / kLanes);
+    const int64_t need = (num_tokens + kTokensPerBlock - 1) / kTokensPerBlock;
+    const dim3 grid((unsigned)(need < 65536 ? need : 65536));
+    const uint16_t* lg = static_cast<const uint16_t*>(logits);
+    uint16_t* w = static_cast<uint16_t*>(weights);
+    switch (k) {
+#define SA_CASE(KK) case KK: hipLaunchKernelGGL((topk_softmax_kernel<E, KK>), grid, dim3(256), 0, stream, lg, num_tokens, indices, w); break;
+        SA_CASE(1) SA_CASE(2) SA_CASE(3) SA_CASE(4) SA_CASE(5) SA_CASE(6) SA_CASE(7) SA_CASE(8)
+#undef SA_CASE
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool topk_softmax_supported(int num_experts) {
+    return num_experts == 8 || num_experts == 16 || num_experts == 32 || num_experts == 64 ||
+           num_experts == 128 || num_experts == 256 || num_experts == 512;
+}
+
+hipError_t launch_topk_softmax(const void* logits, int64_t num_tokens, int num_experts, int k,
+                               int32_t* indices, void* weights, hipStream_t stream) {
+    switch (num_experts) {
+        case 8: return launch_experts<8>(logits, num_tokens, k, indices, weights, stream);
+        case 16: return launch_experts<16>(logits, num_tokens, k, indices, weights, stream);
+        case 32: return launch_experts<32>(logits, num_tokens, k, indices, weights, stream);
+        case 64: return launch_experts<64>(logits, num_tokens, k, indices, weights, stream);
+        case 128: return launch_experts<128>(logits, num_tokens, k, indices, weights, stream);
+        case 256: return launch_experts<256>(logits, num_tokens, k, indices, weights, stream);
+        case 512: return launch_experts<512>(logits, num_tokens, k, indices, weights, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace sa

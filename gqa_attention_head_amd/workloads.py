@@ -245,3 +245,17 @@ def random_case(seed: int, *, dtype="bf16", batch=2, hq=8, hkv=2, d=64, max_q=70
                          seqlens_q=lq, seqlens_k=lk, num_q_heads=hq, num_kv_heads=hkv,
                          head_dim=d, seed=seed, causal=causal, sink_sigma=sink_sigma,
                          sink_values=sink_values, rng=rng)
+
+
+def router_logits(seed: int, tokens: int, experts: int, ties: bool = False) -> tuple[np.ndarray, np.ndarray]:
+    """Seeded router logits for the expert-routing step: bf16 bits [tokens, experts]
+    (uint16) and their exact float32 values.  N(0, 1) draws rounded to bf16, or, with
+    ``ties``, small integers in [-3, 3] (many equal logits) with some -0.0 entries."""
+    rng = np.random.default_rng(seed)
+    if ties:
+        x = rng.integers(-3, 4, size=(tokens, experts)).astype(np.float32)
+        x[rng.random((tokens, experts)) < 0.05] = -0.0
+    else:
+        x = rng.standard_normal((tokens, experts), dtype=np.float32)
+    bits = bf16_round(x)
+    return bits, bf16_widen(bits)

@@ -30,7 +30,8 @@ def declared_functions():
         if fn.endswith(".h"):
             text = open(os.path.join(HEADER_DIR, fn)).read()
             text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-            names += re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(sink_attn_\w+)\s*\(", text, flags=re.M)
+            names += re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b((?:sink_attn|moe)_\w+)\s*\(", text,
+                                flags=re.M)
     return sorted(set(names))
 
 
@@ -230,3 +231,29 @@ def test_split_entry_points_empty_work_needs_no_device(lib):
     """Zero query rows / zero merge rows are valid no-ops (no device touched)."""
     assert _prefill_split(lib, max_q=0) == sa.SA_OK
     assert _merge_rows(lib, rows=0) == sa.SA_OK
+
+
+def _router(lib, **kw):
+    a = dict(logits=P, tokens=1000, experts=128, k=4, idx=P, w=P, stream=NULL)
+    a.update(kw)
+    return lib.moe_topk_softmax(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(logits=NULL), sa.SA_EINVAL),
+    (dict(idx=NULL), sa.SA_EINVAL),
+    (dict(w=NULL), sa.SA_EINVAL),
+    (dict(tokens=-1), sa.SA_EINVAL),
+    (dict(k=0), sa.SA_EINVAL),
+    (dict(k=9), sa.SA_EINVAL),
+    (dict(experts=8, k=8), None),              # valid: checked below without a device
+    (dict(experts=4, k=2), sa.SA_EUNSUPPORTED),
+    (dict(experts=96), sa.SA_EUNSUPPORTED),
+    (dict(experts=1024), sa.SA_EUNSUPPORTED),
+])
+def test_router_rejects(lib, kw, status):
+    if status is None:
+        assert _router(lib, tokens=0, **kw) == sa.SA_OK
+        return
+    assert _router(lib, **kw) == status
+    assert lib.sink_attn_last_error().decode()

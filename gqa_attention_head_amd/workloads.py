@@ -259,3 +259,43 @@ def router_logits(seed: int, tokens: int, experts: int, ties: bool = False) -> t
         x = rng.standard_normal((tokens, experts), dtype=np.float32)
     bits = bf16_round(x)
     return bits, bf16_widen(bits)
+
+
+def yarn_table(rows: int, d: int = 64, *, theta: float = 150000.0, factor: float = 32.0,
+               original_max: int = 4096, beta_fast: float = 32.0, beta_slow: float = 1.0) -> np.ndarray:
+    """Rotary table [rows, d] float32 with YaRN frequency scaling (Peng et al., "YaRN:
+    Efficient Context Window Extension of Large Language Models"): base frequencies
+    theta^(-2i/d); a frequency whose wavelength fits r = original_max / wavelength
+    times into the original context keeps its value when r > beta_fast, is divided by
+    `factor` when r < beta_slow, and is blended linearly in between; cos and sin are
+    multiplied by the attention scale 0.1 ln(factor) + 1.  Row p: cos(p w_i) for
+    i < d/2, then sin(p w_i).  The parameter values are inputs of the workload (the
+    pages name YaRN but give none)."""
+    i = np.arange(d // 2, dtype=np.float64)
+    base = theta ** (-2.0 * i / d)
+    r = original_max * base / (2 * np.pi)
+    keep = np.clip((r - beta_slow) / (beta_fast - beta_slow), 0.0, 1.0)
+    w = base * ((1.0 - keep) / factor + keep)
+    scale = 0.1 * np.log(factor) + 1.0 if factor > 1.0 else 1.0
+    ang = np.arange(rows, dtype=np.float64)[:, None] * w[None, :]
+    return (np.concatenate([np.cos(ang), np.sin(ang)], axis=1) * scale).astype(np.float32)
+
+
+def qkv_epilogue_inputs(seed: int, tokens: int, hq: int, hkv: int, d: int = 64,
+                        max_pos: int = 8192):
+    """Seeded inputs of the bias + rotary epilogue: qkv [tokens, (hq + 2 hkv) d] and
+    bias [(hq + 2 hkv) d] as bf16 bits with their float32 values, positions [tokens]
+    int32 (varlen: sequences of random length restarting at 0), and the YaRN table."""
+    rng = np.random.default_rng(seed)
+    width = (hq + 2 * hkv) * d
+    qkv_bits = bf16_round(rng.standard_normal((tokens, width), dtype=np.float32))
+    bias_bits = bf16_round(0.1 * rng.standard_normal(width, dtype=np.float32))
+    pos = np.empty(tokens, dtype=np.int32)
+    at = 0
+    while at < tokens:
+        n = int(rng.integers(1, min(max_pos, tokens) + 1))
+        n = min(n, tokens - at)
+        pos[at:at + n] = np.arange(n, dtype=np.int32)
+        at += n
+    return (qkv_bits, bf16_widen(qkv_bits), bias_bits, bf16_widen(bias_bits), pos,
+            yarn_table(max_pos, d))

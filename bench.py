@@ -240,6 +240,47 @@ def bench_router(steps: int, warmup: int):
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}}
 
 
+EPILOGUE = dict(tokens=16384, hq=64, hkv=8, max_pos=8192, copies=2)
+
+
+def bench_epilogue(steps: int, warmup: int):
+    """QKV bias + rotary epilogue over 16384 tokens x (64 + 2 x 8) heads of 64 (bf16,
+    two rotated copies of the 168 MB projection output)."""
+    import torch
+    import gqa_attention_head_amd as sa
+    from gqa_attention_head_amd import workloads as W
+
+    t, hq, hkv = EPILOGUE["tokens"], EPILOGUE["hq"], EPILOGUE["hkv"]
+    qkv16, _, b16, _, pos, table = W.qkv_epilogue_inputs(13, t, hq, hkv, 64, EPILOGUE["max_pos"])
+    dev = torch.device("cuda", 0)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    x0 = bf(qkv16)
+    xs = [x0] + [x0.clone() for _ in range(EPILOGUE["copies"] - 1)]
+    bias, pos_d, tab = bf(b16), torch.from_numpy(pos).to(dev), torch.from_numpy(table).to(dev)
+    q = torch.empty(t, hq, 64, device=dev, dtype=torch.bfloat16)
+    k = torch.empty(t, hkv, 64, device=dev, dtype=torch.bfloat16)
+    v = torch.empty(t, hkv, 64, device=dev, dtype=torch.bfloat16)
+    call = lambda i: sa.qkv_bias_rope(xs[i % len(xs)], bias, pos_d, tab, hq, hkv, q=q, k=k, v=v)
+    for i in range(warmup):
+        call(i)
+    _sync()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        call(i)
+    e1.record()
+    _sync()
+    ms = e0.elapsed_time(e1) / steps
+    heads = hq + 2 * hkv
+    # projection output read + q/k/v written + bias + positions + the table rows used
+    nbytes = 2 * t * heads * 64 * 2 + heads * 64 * 2 + t * 4 + len(np.unique(pos)) * 64 * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"qkv_bias_rope_bf16_t{t}_hq{hq}_hkv{hkv}_d64", "ms": round(ms, 5),
+            "roofline": {"kernel": "qkv_rope_kernel", "bound": "hbm", "achieved": round(gbs, 2),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes": int(nbytes)}}
+
+
 def cpu_baseline(dec_wl, pre_wl, budget_s: float = 20.0):
     """The fp64 oracle, untuned, on the host: decode over whole sequences of the decode
     workload, prefill over sampled query rows of the prefill workload."""
@@ -314,7 +355,7 @@ def main(argv=None):
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
-                    help="decode only (skips the prefill, long-KV prefill and router legs)")
+                    help="decode only (skips the prefill, long-KV prefill, router and epilogue legs)")
     args = ap.parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -331,6 +372,7 @@ def main(argv=None):
     pre = None if args.no_prefill else bench_prefill(args.prefill_steps, max(2, args.warmup // 5))
     long_kv = None if args.no_prefill else bench_prefill_long_kv(args.prefill_steps, 2)
     router = None if args.no_prefill else bench_router(50, 5)
+    epilogue = None if args.no_prefill else bench_epilogue(50, 5)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(dec["wl"], pre["wl"] if pre else __import__(
@@ -378,6 +420,8 @@ def main(argv=None):
         line["prefill_long_kv"] = long_kv
     if router is not None:
         line["router"] = router
+    if epilogue is not None:
+        line["qkv_epilogue"] = epilogue
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

@@ -22,7 +22,7 @@ SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_ELAUNCH = 0, 1, 2, 3
 SA_FP32, SA_BF16 = 0, 1
 EXPORTS = ("sink_attn_prefill", "sink_attn_decode_split", "sink_attn_merge",
            "sink_attn_decode", "sink_attn_prefill_split", "sink_attn_merge_rows",
-           "sink_attn_last_error", "moe_topk_softmax")
+           "sink_attn_last_error", "moe_topk_softmax", "qkv_bias_rope")
 
 
 class SinkAttnError(RuntimeError):
@@ -68,6 +68,9 @@ def load_library():
     lib.sink_attn_merge_rows.argtypes = [ctypes.c_int, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.moe_topk_softmax.restype = ctypes.c_int
     lib.moe_topk_softmax.argtypes = [vp, ctypes.c_int64, i32, i32, vp, vp, vp]
+    lib.qkv_bias_rope.restype = ctypes.c_int
+    lib.qkv_bias_rope.argtypes = [vp, vp, vp, vp, ctypes.c_int64, i32, i32, i32, i32, vp, vp, vp,
+                                  vp]
     lib.sink_attn_last_error.restype = ctypes.c_char_p
     lib.sink_attn_last_error.argtypes = []
     _lib = lib
@@ -359,3 +362,40 @@ def topk_softmax(logits, k, indices=None, weights=None, stream=None):
     _check(lib.moe_topk_softmax(_ptr(logits), t, e, int(k), _ptr(indices), _ptr(weights),
                                 _stream(stream)))
     return indices, weights
+
+
+def qkv_bias_rope(qkv, bias, positions, cos_sin, num_q_heads, num_kv_heads, q=None, k=None,
+                  v=None, stream=None):
+    """Pre-attention epilogue (``qkv_bias_rope``): fused projection output qkv
+    [T, (Hq + 2 Hkv) * 64] bf16 plus bias, rotary embedding on the query and key heads from
+    the cos/sin table [rows, 64] float32 at each token's position -> (q [T, Hq, 64],
+    k [T, Hkv, 64], v [T, Hkv, 64]) bf16."""
+    torch = _torch()
+    lib = load_library()
+    d = 64
+    heads = num_q_heads + 2 * num_kv_heads
+    _dev(qkv, "qkv", torch.bfloat16)
+    _dev(bias, "bias", torch.bfloat16)
+    _dev(positions, "positions", torch.int32)
+    _dev(cos_sin, "cos_sin", torch.float32)
+    if qkv.dim() != 2 or qkv.shape[1] != heads * d:
+        raise ValueError(f"qkv must be [T, {heads * d}]")
+    if bias.numel() != heads * d:
+        raise ValueError(f"bias must hold {heads * d} values")
+    t = qkv.shape[0]
+    if positions.numel() != t:
+        raise ValueError("positions must be [T]")
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != d:
+        raise ValueError("cos_sin must be [rows, 64]")
+    outs = []
+    for name, buf, h in (("q", q, num_q_heads), ("k", k, num_kv_heads), ("v", v, num_kv_heads)):
+        if buf is None:
+            buf = torch.empty(t, h, d, device=qkv.device, dtype=torch.bfloat16)
+        _dev(buf, name, torch.bfloat16)
+        if tuple(buf.shape) != (t, h, d):
+            raise ValueError(f"{name} must be [T, {h}, {d}]")
+        outs.append(buf)
+    _check(lib.qkv_bias_rope(_ptr(qkv), _ptr(bias), _ptr(positions), _ptr(cos_sin), t,
+                             num_q_heads, num_kv_heads, d, cos_sin.shape[0], _ptr(outs[0]),
+                             _ptr(outs[1]), _ptr(outs[2]), _stream(stream)))
+    return tuple(outs)

@@ -4,12 +4,15 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <initializer_list>
 #include <string>
 
 #include "kernels.h"
 #include "moe_router.h"
+#include "qkv_epilogue.h"
 #include "sink_attn.h"
 
 namespace {
@@ -69,6 +72,15 @@ sa_status_t check_heads(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim
     return SA_OK;
 }
 
+// A launch's x dimension counts work-items in 32 bits: blocks * threads per block
+// must stay below 2^32.
+sa_status_t check_grid(int64_t blocks, int64_t threads_per_block, const char* what) {
+    if (blocks > 0 && blocks > (int64_t)0xFFFFFFFFLL / threads_per_block)
+        return fail(SA_EINVAL, "%s: %lld blocks of %lld threads exceed the 2^32 work-item grid limit",
+                    what, (long long)blocks, (long long)threads_per_block);
+    return SA_OK;
+}
+
 sa_status_t check_dtype(sa_dtype_t d) {
     if (d != SA_FP32 && d != SA_BF16) return fail(SA_EINVAL, "unknown dtype %d", (int)d);
     return SA_OK;
@@ -96,12 +108,17 @@ sa_status_t sink_attn_prefill(sa_dtype_t dtype, const void* q, const void* k, co
     if (causal != 0 && causal != 1) return fail(SA_EINVAL, "causal must be 0 or 1");
     if (!(std::isfinite(sm_scale) && sm_scale > 0.0f))
         return fail(SA_EINVAL, "sm_scale must be finite and > 0");
+    const int group = num_q_heads / num_kv_heads;
+    const bool mfma = dtype == SA_BF16 && sa::mfma_prefill_supported(group);
+    if (mfma && (s = check_grid((int64_t)batch * num_kv_heads * ((max_seqlen_q + 31) / 32),
+                                64 * group, "sink_attn_prefill")) != SA_OK)
+        return s;
+    if (!mfma && (s = check_grid(max_seqlen_q, 64, "sink_attn_prefill")) != SA_OK) return s;
     if (max_seqlen_q == 0) return ok();
     if ((s = check_device()) != SA_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const int group = num_q_heads / num_kv_heads;
     hipError_t e;
-    if (dtype == SA_BF16 && sa::mfma_prefill_supported(group))
+    if (mfma)
         e = sa::launch_mfma_prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, batch, num_q_heads,
                                     num_kv_heads, max_seqlen_q, sm_scale, causal, out, lse, st);
     else
@@ -138,10 +155,13 @@ sa_status_t sink_attn_prefill_split(sa_dtype_t dtype, const void* q, const void*
     const int group = num_q_heads / num_kv_heads;
     const bool mfma = dtype == SA_BF16 && sa::mfma_prefill_supported(group);
     if (mfma) {
-        if ((int64_t)batch * num_kv_heads * ((max_seqlen_q + 31) / 32) * max_num_chunks > 0x7fffffffLL)
-            return fail(SA_EINVAL, "batch * Hkv * query blocks * max_num_chunks exceeds the grid limit");
+        if ((s = check_grid((int64_t)batch * num_kv_heads * ((max_seqlen_q + 31) / 32) * max_num_chunks,
+                            64 * group, "sink_attn_prefill_split")) != SA_OK)
+            return s;
     } else if ((int64_t)batch * max_num_chunks > 65535) {
         return fail(SA_EINVAL, "batch * max_num_chunks must be <= 65535 on this path");
+    } else if ((s = check_grid(max_seqlen_q, 64, "sink_attn_prefill_split")) != SA_OK) {
+        return s;
     }
     if (max_seqlen_q == 0) return ok();
     if ((s = check_device()) != SA_OK) return s;
@@ -172,8 +192,8 @@ sa_status_t sink_attn_merge_rows(sa_dtype_t out_dtype, const float* part_m, cons
     if (num_q_heads < 1) return fail(SA_EINVAL, "num_q_heads must be >= 1");
     if (head_dim != 64) return fail(SA_EUNSUPPORTED, "head_dim %d is not supported (only 64)", head_dim);
     if (max_num_chunks < 1) return fail(SA_EINVAL, "max_num_chunks must be >= 1");
-    if ((int64_t)num_rows * num_q_heads > 0x7fffffffLL)
-        return fail(SA_EINVAL, "num_rows * num_q_heads exceeds the grid limit");
+    if ((s = check_grid(((int64_t)num_rows * num_q_heads + 3) / 4, 256, "sink_attn_merge_rows")) != SA_OK)
+        return s;
     if (num_rows == 0) return ok();
     if ((s = check_device()) != SA_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -205,8 +225,8 @@ sa_status_t check_split_args(sa_dtype_t dtype, const void* q, const void* k, con
                     max_num_chunks, (long long)need);
     if (!(std::isfinite(sm_scale) && sm_scale > 0.0f))
         return fail(SA_EINVAL, "sm_scale must be finite and > 0");
-    if ((int64_t)batch * max_num_chunks * num_kv_heads > 0x7fffffffLL)
-        return fail(SA_EINVAL, "batch * max_num_chunks * Hkv exceeds the grid limit");
+    if ((s = check_grid((int64_t)batch * max_num_chunks * ((num_kv_heads + 7) / 8), 512, "decode")) != SA_OK)
+        return s;
     return SA_OK;
 }
 
@@ -278,8 +298,8 @@ sa_status_t sink_attn_merge(sa_dtype_t out_dtype, const float* part_m, const flo
         return fail(SA_EINVAL, "sink_attn_merge: null pointer argument");
     if (batch < 1 || batch > 65535) return fail(SA_EINVAL, "batch must be in [1, 65535], got %d", batch);
     if (num_q_heads < 1) return fail(SA_EINVAL, "num_q_heads must be >= 1");
-    if ((int64_t)batch * num_q_heads > 0x7fffffffLL)
-        return fail(SA_EINVAL, "batch * num_q_heads exceeds the grid limit");
+    if ((s = check_grid(((int64_t)batch * num_q_heads + 3) / 4, 256, "sink_attn_merge")) != SA_OK)
+        return s;
     if (head_dim != 64) return fail(SA_EUNSUPPORTED, "head_dim %d is not supported (only 64)", head_dim);
     if (kv_chunk_size < 1) return fail(SA_EINVAL, "kv_chunk_size must be >= 1, got %d", kv_chunk_size);
     if (max_num_chunks < 1) return fail(SA_EINVAL, "max_num_chunks must be >= 1");
@@ -304,6 +324,32 @@ sa_status_t moe_topk_softmax(const void* logits, int64_t num_tokens, int32_t num
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = sa::launch_topk_softmax(logits, num_tokens, num_experts, k, indices, weights, st);
     return finish_launch(e, st, "moe_topk_softmax");
+}
+
+sa_status_t qkv_bias_rope(const void* qkv, const void* bias, const int32_t* positions,
+                          const float* cos_sin, int64_t num_tokens, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t table_rows, void* q,
+                          void* k, void* v, void* stream) {
+    if (num_tokens < 0) return fail(SA_EINVAL, "num_tokens must be >= 0");
+    if (num_q_heads < 1 || num_kv_heads < 1) return fail(SA_EINVAL, "head counts must be >= 1");
+    if (head_dim != 64) return fail(SA_EUNSUPPORTED, "head_dim %d is not supported (only 64)", head_dim);
+    if (table_rows < 1) return fail(SA_EINVAL, "table_rows must be >= 1");
+    const int64_t heads = (int64_t)num_q_heads + 2 * (int64_t)num_kv_heads;
+    sa_status_t s;
+    // one thread per quarter head: num_tokens * heads * 4 work-items, below 2^32
+    if (num_tokens > (int64_t)0xFFFFFFFFLL / (heads * 4))
+        return fail(SA_EINVAL, "qkv_bias_rope: num_tokens * heads * 4 exceeds the 2^32 work-item grid limit");
+    if (num_tokens == 0) return ok();  // nothing to read or write: pointers may be null
+    if (!qkv || !bias || !positions || !cos_sin || !q || !k || !v)
+        return fail(SA_EINVAL, "qkv_bias_rope: null pointer argument");
+    for (const void* p : {qkv, bias, (const void*)cos_sin, (const void*)q, (const void*)k, (const void*)v})
+        if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+            return fail(SA_EINVAL, "qkv_bias_rope: qkv, bias, cos_sin, q, k and v must be 16-byte aligned");
+    if ((s = check_device()) != SA_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = sa::launch_qkv_rope(qkv, bias, positions, cos_sin, num_tokens, num_q_heads,
+                                       num_kv_heads, table_rows, q, k, v, st);
+    return finish_launch(e, st, "qkv_bias_rope");
 }
 
 }  // extern "C"

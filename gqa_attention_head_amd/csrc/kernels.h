@@ -49,6 +49,11 @@ bool topk_softmax_supported(int num_experts);
 hipError_t launch_topk_softmax(const void* logits, int64_t num_tokens, int num_experts, int k,
                                int32_t* indices, void* weights, hipStream_t stream);
 
+// Bias add + rotary embedding of the fused QKV projection output (bf16, D = 64).
+hipError_t launch_qkv_rope(const void* qkv, const void* bias, const int32_t* positions,
+                           const float* cos_sin, int64_t num_tokens, int hq, int hkv, int rows,
+                           void* q, void* k, void* v, hipStream_t stream);
+
 // Log-sum-exp combination of split-KV chunk states.  cu_k == nullptr: every
 // one of the max_chunks slots of each of the `batch` rows is combined.
 hipError_t launch_merge(bool out_bf16, const float* part_m, const float* part_d,

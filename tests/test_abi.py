@@ -30,7 +30,7 @@ def declared_functions():
         if fn.endswith(".h"):
             text = open(os.path.join(HEADER_DIR, fn)).read()
             text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-            names += re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b((?:sink_attn|moe)_\w+)\s*\(", text,
+            names += re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b((?:sink_attn|moe|qkv)_\w+)\s*\(", text,
                                 flags=re.M)
     return sorted(set(names))
 
@@ -257,3 +257,33 @@ def test_router_rejects(lib, kw, status):
         return
     assert _router(lib, **kw) == status
     assert lib.sink_attn_last_error().decode()
+
+
+def _rope(lib, **kw):
+    a = dict(qkv=P, bias=P, pos=P, cs=P, tokens=1000, hq=64, hkv=8, d=64, rows=4096, q=P, k=P,
+             v=P, stream=NULL)
+    a.update(kw)
+    return lib.qkv_bias_rope(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qkv=NULL), sa.SA_EINVAL),
+    (dict(bias=NULL), sa.SA_EINVAL),
+    (dict(pos=NULL), sa.SA_EINVAL),
+    (dict(cs=NULL), sa.SA_EINVAL),
+    (dict(v=NULL), sa.SA_EINVAL),
+    (dict(tokens=-1), sa.SA_EINVAL),
+    (dict(hq=0), sa.SA_EINVAL),
+    (dict(hkv=0), sa.SA_EINVAL),
+    (dict(rows=0), sa.SA_EINVAL),
+    (dict(d=128), sa.SA_EUNSUPPORTED),
+    (dict(k=ctypes.c_void_p(264)), sa.SA_EINVAL),   # not 16-byte aligned
+    (dict(tokens=1 << 40), sa.SA_EINVAL),       # grid beyond 2^31 - 1 blocks
+])
+def test_qkv_bias_rope_rejects(lib, kw, status):
+    assert _rope(lib, **kw) == status
+    assert lib.sink_attn_last_error().decode()
+
+
+def test_qkv_bias_rope_empty_is_a_no_op(lib):
+    assert _rope(lib, tokens=0, qkv=NULL, q=NULL) == sa.SA_OK

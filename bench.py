@@ -137,20 +137,42 @@ def bench_prefill(steps: int, warmup: int):
     def step():
         sa.prefill(q, k, v, sinks, cu_q, cu_k, lq, lq, wl.sm_scale, causal=True, out=out, lse=lse)
 
-    for _ in range(warmup):
+    # The clock needs some tens of milliseconds of load to settle after idle: the
+    # warm-up runs at least 50 launches (about 30 ms) before the timed run.
+    for _ in range(max(warmup, 50)):
         step()
     _sync()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    for i in range(steps):
-        evs[i][0].record()
+    # back-to-back launches between one event pair on the launch stream
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(steps):
         step()
-        evs[i][1].record()
+    ev[1].record()
     _sync()
-    ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    mean_ms = ev[0].elapsed_time(ev[1]) / steps
     flops = wl.prefill_flops()
-    mean_ms = float(ms.mean())
-    return dict(workload=wl.name, flops=flops, ms_mean=mean_ms, ms_median=float(np.median(ms)),
-                tflops=flops / (mean_ms * 1e-3) / 1e12, wl=wl)
+    return dict(workload=wl.name, flops=flops, ms_mean=mean_ms,
+                tflops=flops / (mean_ms * 1e-3) / 1e12, wl=wl, gemm_tflops=library_gemm_tflops())
+
+
+def library_gemm_tflops(n: int = 8192, steps: int = 50, warmup: int = 20) -> float:
+    """Context for the MFMA roofline: what the vendor GEMM (torch.matmul -> hipBLASLt)
+    sustains on a square bf16 n x n x n product on this GPU, right after the prefill."""
+    import torch
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(warmup):
+        torch.matmul(a, b, out=c)
+    _sync()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(steps):
+        torch.matmul(a, b, out=c)
+    ev[1].record()
+    _sync()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
 
 
 LONG_KV = dict(lq=256, lk=131072, chunk=16384)  # chunked prefill over a long cache
@@ -351,8 +373,8 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--prefill-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="decode only (skips the prefill, long-KV prefill, router and epilogue legs)")
@@ -369,10 +391,10 @@ def main(argv=None):
     torch.cuda.set_device(0)
 
     dec = bench_decode(args.steps, args.warmup)
-    pre = None if args.no_prefill else bench_prefill(args.prefill_steps, max(2, args.warmup // 5))
-    long_kv = None if args.no_prefill else bench_prefill_long_kv(args.prefill_steps, 2)
-    router = None if args.no_prefill else bench_router(50, 5)
-    epilogue = None if args.no_prefill else bench_epilogue(50, 5)
+    pre = None if args.no_prefill else bench_prefill(args.prefill_steps, 50)
+    long_kv = None if args.no_prefill else bench_prefill_long_kv(max(10, args.prefill_steps // 2), 20)
+    router = None if args.no_prefill else bench_router(200, 50)
+    epilogue = None if args.no_prefill else bench_epilogue(200, 50)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(dec["wl"], pre["wl"] if pre else __import__(
@@ -415,7 +437,11 @@ def main(argv=None):
             "roofline": {"kernel": "prefill_mfma<8, false>", "bound": "mfma",
                          "achieved": round(pre["tflops"], 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(pre["tflops"] / BF16_PEAK_TFLOPS, 4),
-                         "traffic": traffic.get("prefill"), "algorithmic_flops": pre["flops"]}}
+                         "traffic": traffic.get("prefill"), "algorithmic_flops": pre["flops"]},
+            "context_vendor_gemm_bf16_8192": {
+                "tflops": round(pre["gemm_tflops"], 1),
+                "frac_of_peak": round(pre["gemm_tflops"] / BF16_PEAK_TFLOPS, 4),
+                "prefill_over_gemm": round(pre["tflops"] / pre["gemm_tflops"], 4)}}
     if long_kv is not None:
         line["prefill_long_kv"] = long_kv
     if router is not None:

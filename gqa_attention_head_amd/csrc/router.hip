@@ -8,14 +8,15 @@
 //
 // Layout: a token's E logits are spread over E/32 lanes (one lane for E < 32),
 // each reading its 32 (or E) logits as 16-byte loads, so a wave's loads cover a
-// contiguous run of whole token rows.  Each logit becomes one 32-bit key whose unsigned
-// order is the ranking: the high half is the bf16 bit pattern mapped to an
-// order-preserving unsigned code (-0 folded onto +0), the low half is
-// 0xFFFF - expert, so a larger key is a larger logit or, on a tie, a lower
-// expert index.  Each lane sorts its keys in groups of 8 and keeps its K
-// largest (bitonic merges); round r then takes the largest head key across the
-// token's lanes (DPP and lane-swap maxima, no LDS), and the lane that held it
-// moves on to its next key.
+// contiguous run of whole token rows.  Each logit becomes one 32-bit key whose
+// unsigned order is the ranking: the high half maps the bf16 value to an
+// order-preserving code (-0 folded onto +0; two codes per word with packed 16-bit
+// arithmetic), the low half holds 31 - (position in the lane), so a larger key is
+// a larger logit or, on a tie, a lower expert.  Each lane inserts its keys into a
+// descending list of its KP largest (one max and KP - 1 three-way medians per
+// key), then turns the low halves into 0xFFFF - expert; round r takes the largest
+// head across the token's lanes (DPP and lane-swap maxima, no LDS), and the lane
+// that held it moves on to its next key.
 #include <type_traits>
 
 #include "common.h"
@@ -53,43 +54,29 @@ __device__ __forceinline__ uint32_t group_max(uint32_t x) {
 
 constexpr int next_pow2(int k) { return k <= 1 ? 1 : (k <= 2 ? 2 : (k <= 4 ? 4 : 8)); }
 
-// Sorts 8 keys in registers, descending (odd-even merge network, 19 exchanges).
-__device__ __forceinline__ void sort8(uint32_t* x) {
-    auto cx = [&](int a, int b) {
-        const uint32_t hi = max(x[a], x[b]), lo = min(x[a], x[b]);
-        x[a] = hi;
-        x[b] = lo;
-    };
-    cx(0, 1); cx(2, 3); cx(4, 5); cx(6, 7);
-    cx(0, 2); cx(1, 3); cx(4, 6); cx(5, 7);
-    cx(1, 2); cx(5, 6);
-    cx(0, 4); cx(1, 5); cx(2, 6); cx(3, 7);
-    cx(2, 4); cx(3, 5);
-    cx(1, 2); cx(3, 4); cx(5, 6);
+// Median of three unsigned words (v_med3_u32).
+__device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t r;
+    asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
 }
 
-// top: the KP largest keys seen so far, descending; g: 8 more keys, descending.
-// Afterwards top holds the KP largest of both, descending (the pairwise maxima
-// of top and reversed g form a bitonic sequence, sorted by a bitonic merge).
-template <int KP>
-__device__ __forceinline__ void merge_top(uint32_t* top, const uint32_t* g) {
-#pragma unroll
-    for (int i = 0; i < KP; ++i) top[i] = max(top[i], g[KP - 1 - i]);
-#pragma unroll
-    for (int half = KP / 2; half >= 1; half /= 2)
-#pragma unroll
-        for (int i = 0; i < KP; ++i)
-            if ((i & half) == 0) {
-                const uint32_t hi = max(top[i], top[i + half]), lo = min(top[i], top[i + half]);
-                top[i] = hi;
-                top[i + half] = lo;
-            }
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+
+// Order codes of the two bf16 values of a word, in place: 0x8000 + m for +m and
+// 0x8000 - m for -m (so -0 and +0 share 0x8000), computed with packed 16-bit ops.
+__device__ __forceinline__ uint32_t order_codes(uint32_t w) {
+    const u16x2 x = __builtin_bit_cast(u16x2, w);
+    const u16x2 s = __builtin_bit_cast(u16x2, __builtin_bit_cast(i16x2, x) >> (int16_t)15);
+    const u16x2 mag = (x ^ s) - s;  // 0 - x for negative values, x otherwise
+    return __builtin_bit_cast(uint32_t, mag) ^ (~__builtin_bit_cast(uint32_t, s) & 0x80008000u);
 }
 
 // One token's E logits are spread over kLanes = E / kPer lanes, kPer = min(E, 32)
 // logits (kPer / 8 16-byte loads) per lane; a wave handles 64 / kLanes tokens per
-// step.  Each lane keeps its KP = next_pow2(K) largest keys, then K rounds pick the
-// largest head across the token's lanes.
+// step.  Each lane keeps its KP = next_pow2(K) largest keys (KP <= 8 <= kPer), then
+// K rounds pick the largest head across the token's lanes.
 template <int E, int K>
 __global__ __launch_bounds__(256) void topk_softmax_kernel(const uint16_t* __restrict__ logits,
                                                            int64_t num_tokens,
@@ -118,25 +105,31 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const uint16_t* __res
         }
         uint32_t top[KP];
 #pragma unroll
+        for (int i = 0; i < KP; ++i) top[i] = 0u;  // below every key
+#pragma unroll
         for (int q = 0; q < kGroups; ++q) {
-            uint32_t key[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                // bf16 bits in the high half: H.  The key's high half is the order code
-                // (0x8000 + m for +m, 0x8000 - m for -m, so -0 ranks with +0); its low
-                // half is 0xFFFF - expert.
-                const uint32_t h = (j % 2) ? (raw[q][j / 2] & 0xFFFF0000u) : (raw[q][j / 2] << 16);
-                const uint32_t idc = 0xFFFFu - (uint32_t)(kPer * sub + 8 * q + j);
-                key[j] = (h > 0x80000000u) ? (idc - h) : (h | 0x80000000u | idc);
-            }
-            sort8(key);
-            if (q == 0) {
+            for (int e = 0; e < 4; ++e) {
+                // low half: 31 - (position in the lane); made global after selection
+                const uint32_t code = order_codes(raw[q][e]);
+                const uint32_t key_lo = (code << 16) | (uint32_t)(31 - (8 * q + 2 * e));
+                const uint32_t key_hi = (code & 0xFFFF0000u) | (uint32_t)(30 - (8 * q + 2 * e));
 #pragma unroll
-                for (int i = 0; i < KP; ++i) top[i] = key[i];
-            } else {
-                merge_top<KP>(top, key);
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const uint32_t x = h2 ? key_hi : key_lo;
+                    // insert x into the descending list: entry i becomes the median of
+                    // old entries i-1, i and x (the list's top: the larger of two)
+#pragma unroll
+                    for (int i = KP - 1; i >= 1; --i) top[i] = med3_u32(top[i - 1], top[i], x);
+                    top[0] = max(top[0], x);
+                }
             }
         }
+        // low half 31 - pos becomes 0xFFFF - expert with expert = kPer * sub + pos (no
+        // carry); every entry is a real key, since KP <= 8 <= kPer
+        const uint32_t to_global = 0xFFFFu - (uint32_t)(kPer * sub) - 31u;
+#pragma unroll
+        for (int i = 0; i < KP; ++i) top[i] += to_global;
         // round r: the largest head among the token's lanes wins; its lane moves on
         uint32_t win[K];
 #pragma unroll

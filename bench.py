@@ -346,6 +346,8 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_decode_b32_kv4096_pref
 TRAFFIC_SOURCES = {
     "decode": ("gqa_attention_head_amd/csrc/common.h", "gqa_attention_head_amd/csrc/decode.hip"),
     "prefill": ("gqa_attention_head_amd/csrc/common.h", "gqa_attention_head_amd/csrc/prefill.hip"),
+    "router": ("gqa_attention_head_amd/csrc/common.h", "gqa_attention_head_amd/csrc/router.hip"),
+    "epilogue": ("gqa_attention_head_amd/csrc/common.h", "gqa_attention_head_amd/csrc/epilogue.hip"),
 }
 
 
@@ -445,8 +447,10 @@ def main(argv=None):
     if long_kv is not None:
         line["prefill_long_kv"] = long_kv
     if router is not None:
+        router["roofline"]["traffic"] = traffic.get("router")
         line["router"] = router
     if epilogue is not None:
+        epilogue["roofline"]["traffic"] = traffic.get("epilogue")
         line["qkv_epilogue"] = epilogue
     if cpu is not None:
         line["cpu_baseline"] = cpu

@@ -16,7 +16,8 @@
 // Per 64-key tile and wave (scores kept transposed, S^T = K Q^T, so that the
 // exponentiated tile is already laid out as the B operand of the PV product):
 //   S^T[64 keys x 32 rows] = K[64 x 64] . Q^T[64 x 32]      8 MFMA 32x32x16
-//   bottom-right causal mask on diagonal tiles, online softmax in base 2
+//   bottom-right causal mask on diagonal tiles, online softmax in base 2 (the
+//   row maximum is taken only when the running one is too low: see kSumLimit)
 //   O^T[64 dims x 32 rows] += V^T[64 x 64] . P^T[64 x 32]   8 MFMA 32x32x16
 //     (V read transposed out of LDS with ds_read_b64_tr_b16)
 // K/V tiles are double-buffered: the next tile's global loads are in flight
@@ -37,10 +38,34 @@ constexpr int kStride = kD + 8;     // LDS row stride of K tiles in bf16 element
 constexpr int kVStride = kD + 32;
 constexpr int kSegs = kBK * kD / 8; // 16-byte segments per K (or V) tile
 
-// Above this growth of the row maximum (base-2 units) the running state is
-// rescaled; smaller growth keeps the stale maximum, so exponentiated scores stay
-// below 2^kRescaleThreshold and the rescale multiply is skipped for the tile.
-constexpr float kRescaleThreshold = 8.0f;
+// Exponentials are first taken against the running maximum m as it stands.  If a
+// lane's sum of its 32 exponentials stays within kSumLimit, each of them does too
+// (they are positive), the state needs no rescale and the tile skips the row-max
+// reduction.  Otherwise (a score far above m, or an overflow) the tile takes its
+// row maximum, rescales the state and exponentiates again.
+constexpr float kSumLimit = 16384.0f;  // 2^14
+
+// P^T tile in bf16, four 16-key slices (the B operand of O^T = V^T P^T): the
+// exponentials 2^(s * scale_log2 - msub) of one lane's 32 scores; returns their
+// fp32 sum (the lane's share of the running scale).
+__device__ __forceinline__ float exp_tile(const f32x16 (&s)[2], float scale_log2, float msub,
+                                          bf16x8 (&pb)[4]) {
+    float psum = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int kb = ks / 2, hs = ks % 2;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * hs + 2 * e], scale_log2, -msub));
+            const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * hs + 2 * e + 1], scale_log2, -msub));
+            const bf16x2 pk = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+            pb[ks][2 * e] = pk[0];
+            pb[ks][2 * e + 1] = pk[1];
+            psum += p0 + p1;
+        }
+    }
+    return psum;
+}
 
 // kSplit: the keys of each sequence are cut into chunks of `chunk` keys, one
 // chunk per launch index (the slowest grid dimension), and the kernel writes each
@@ -164,61 +189,52 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
         const uint16_t* kt = kl[buf];
         const uint16_t* vt = vl[buf];
 
-        // raw scores: s[kb][i] = <q_row, k_key>, key = j0 + 32*kb + 8*(i/4) + 4*half + i%4
+        // raw scores: s[kb][i] = <q_row, k_key>, key = j0 + 32*kb + 8*(i/4) + 4*half + i%4,
+        // keys outside [k_lo, row_lim) masked to -inf on an edge tile (diagonal, ragged
+        // or chunk edge; uniform).  A macro rather than a function: this kernel sits at
+        // the 128-VGPR limit, and the function form made the compiler spill.
+#define SA_SCORES()                                                                              \
+    _Pragma("unroll") for (int kb = 0; kb < 2; ++kb) {                                           \
+        _Pragma("unroll") for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;                          \
+        _Pragma("unroll") for (int ks = 0; ks < 4; ++ks) {                                       \
+            const bf16x8 a = load_bf16x8(kt + (32 * kb + l32) * kStride + 16 * ks + 8 * half);   \
+            s[kb] = mfma32x32x16(a, qop[ks], s[kb]);                                             \
+        }                                                                                        \
+    }                                                                                            \
+    if (j0 + kBK > full_end || j0 < k_lo) {                                                      \
+        _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                         \
+        _Pragma("unroll") for (int i = 0; i < 16; ++i) {                                         \
+            const int key = j0 + 32 * kb + 8 * (i / 4) + 4 * half + (i % 4);                     \
+            if (key >= row_lim || key < k_lo) s[kb][i] = kNegInf;                                \
+        }                                                                                        \
+    }
         f32x16 s[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 a = load_bf16x8(kt + (32 * kb + l32) * kStride + 16 * ks + 8 * half);
-                s[kb] = mfma32x32x16(a, qop[ks], s[kb]);
-            }
+        SA_SCORES()
+        bf16x8 pb[4];
+        float psum;
+        // no finite reference yet (no sink and no visible key so far): take the max
+        bool need_max = __any(m == kNegInf);
+        if (!need_max) {
+            psum = exp_tile(s, scale_log2, m, pb);
+            need_max = __any(!(psum <= kSumLimit));
         }
-        if (j0 + kBK > full_end || j0 < k_lo) {  // diagonal, ragged or chunk-edge tile (uniform)
+        if (need_max) {  // rare: recompute the scores rather than keep them live
+            SA_SCORES()
+            float tmax = kNegInf;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = j0 + 32 * kb + 8 * (i / 4) + 4 * half + (i % 4);
-                    if (key >= row_lim || key < k_lo) s[kb][i] = kNegInf;
-                }
-        }
-        // row max of the tile (sm_scale > 0, so the max of raw scores scales)
-        float tmax = kNegInf;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kb][i]);
-        const float m_cand = max_xor32(tmax) * scale_log2;
-        if (__any(m_cand > m + kRescaleThreshold)) {
-            const float m_new = fmaxf(m, m_cand);
+                for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kb][i]);
+            const float m_new = fmaxf(m, max_xor32(tmax) * scale_log2);
             const float alpha = (m == kNegInf) ? 0.0f : fast_exp2(m - m_new);
             dl *= alpha;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) o[mt] *= alpha;
             m = m_new;
+            const float msub = (m == kNegInf) ? 0.0f : m;
+            psum = exp_tile(s, scale_log2, msub, pb);
         }
-        const float msub = (m == kNegInf) ? 0.0f : m;
-
-        // P^T tile in bf16, four 16-key slices (the B operand of O^T = V^T P^T);
-        // the running scale accumulates the exponentials in fp32.
-        bf16x8 pb[4];
-        float psum = 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int kb = ks / 2, hs = ks % 2;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * hs + 2 * e], scale_log2, -msub));
-                const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * hs + 2 * e + 1], scale_log2, -msub));
-                const bf16x2 pk = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
-                pb[ks][2 * e] = pk[0];
-                pb[ks][2 * e + 1] = pk[1];
-                psum += p0 + p1;
-            }
-        }
+#undef SA_SCORES
         dl += psum;
 
 #pragma unroll

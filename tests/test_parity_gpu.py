@@ -210,6 +210,35 @@ def test_log2_domain_sinks(orc):
     H.assert_lse_close(dlse, dref_lse, bf16=True)
 
 
+@pytest.mark.parametrize("ramp", ["rising", "falling"])
+def test_running_max_growth(orc, ramp):
+    """Scores whose scale grows (or shrinks) along the keys: with a rising ramp each row's
+    maximum keeps climbing far past the running one (many rescales, also mid-sequence and
+    after a sink that was the maximum); with a falling ramp the first tile sets the
+    maximum for good.  Sinks cover -inf, large negative, zero and large positive."""
+    rng = np.random.default_rng(65)
+    lq, lk = 96, 700
+    wl = W.make_workload(f"ramp_{ramp}", dtype="bf16", kind="prefill", seqlens_q=[lq, 1],
+                         seqlens_k=[lk, lk], num_q_heads=8, num_kv_heads=2, head_dim=64, seed=65,
+                         causal=True,
+                         sink_values=[float("-inf"), -20.0, 0.0, 20.0, 3.0, float("-inf"), 40.0, -3.0],
+                         rng=rng)
+    j = np.arange(wl.k32.shape[0]) % lk
+    f = 1.0 + 24.0 * j / lk if ramp == "rising" else 25.0 - 24.0 * j / lk
+    wl.k16 = W.bf16_round((wl.k32 * f[:, None, None]).astype(np.float32))
+    wl.k32 = W.bf16_widen(wl.k16)
+    wl.q16 = W.bf16_round(wl.q32 * 2.0)
+    wl.q32 = W.bf16_widen(wl.q16)
+    dev = H.Device(wl)
+    out, lse = H.run_prefill(dev)
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    H.assert_close(out, ref, bf16=True)
+    H.assert_lse_close(lse, ref_lse, bf16=True)
+    _, _, _, mout, mlse = run_prefill_split(dev, 128)
+    H.assert_close(mout, ref, bf16=True)
+    H.assert_lse_close(mlse, ref_lse, bf16=True)
+
+
 def test_prefill_rows_equal_decode(orc):
     """Row i of a causal prefill equals a decode of that query over its visible keys."""
     wl = W.make_workload("pd", dtype="bf16", kind="prefill", seqlens_q=[70], seqlens_k=[250],

@@ -106,12 +106,21 @@ def bench_decode(steps: int, warmup: int):
         graphs[i % KV_COPIES].replay()
     _sync()
     graph_ms = (time.perf_counter() - t0) * 1e3 / steps
+    # distribution of single steps (an event pair around each step adds its own gap)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        step(i)
+        evs[i][1].record()
+    _sync()
+    step_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     kv_bytes = wl.kv_bytes()
     ms_per_step = wall2 * 1e3 / steps
     return dict(
         workload=wl.name, kv_bytes=kv_bytes, ms_per_step=ms_per_step,
         gbs=kv_bytes / (ms_per_step * 1e-3) / 1e9,
         split_ms_mean=float(split_ms), graph_ms_per_step=graph_ms,
+        step_ms_p10_p50_p90=[float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
         batch=wl.batch, kv_len=int(max_lk), chunk=chunk, num_chunks=nch, wl=wl)
 
 
@@ -150,9 +159,41 @@ def bench_prefill(steps: int, warmup: int):
     ev[1].record()
     _sync()
     mean_ms = ev[0].elapsed_time(ev[1]) / steps
+    # distribution of single launches (an event pair around each)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        step()
+        evs[i][1].record()
+    _sync()
+    one = np.array([e[0].elapsed_time(e[1]) for e in evs])
     flops = wl.prefill_flops()
     return dict(workload=wl.name, flops=flops, ms_mean=mean_ms,
+                ms_p10_p50_p90=[float(np.percentile(one, q)) for q in (10, 50, 90)],
                 tflops=flops / (mean_ms * 1e-3) / 1e12, wl=wl, gemm_tflops=library_gemm_tflops())
+
+
+def context_hbm():
+    """Context for the HBM roofline: what torch's own kernels sustain on this GPU, a
+    reduction (reads 2 GiB) and a copy (reads and writes 1 GiB)."""
+    import torch
+    x = torch.ones(1 << 30, device="cuda", dtype=torch.bfloat16)
+    y = torch.empty(1 << 29, device="cuda", dtype=torch.bfloat16)
+    res = {}
+    for name, fn, nbytes in (("sum_read_gbs", lambda: x.sum(dtype=torch.float32), 2 << 30),
+                             ("copy_gbs", lambda: y.copy_(x[: 1 << 29]), 2 << 30)):
+        for _ in range(5):
+            fn()
+        _sync()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(20):
+            fn()
+        ev[1].record()
+        _sync()
+        res[name] = round(nbytes / (ev[0].elapsed_time(ev[1]) / 20 * 1e-3) / 1e9, 1)
+    del x, y
+    return res
 
 
 def library_gemm_tflops(n: int = 8192, steps: int = 50, warmup: int = 20) -> float:
@@ -333,13 +374,63 @@ def cpu_baseline(dec_wl, pre_wl, budget_s: float = 20.0):
         i = int(r - pre_wl.cu_q[b])
         pairs += int(pre_wl.seqlens_k[b]) - int(pre_wl.seqlens_q[b]) + i + 1
     pre_flops = 4 * pre_wl.head_dim * pre_wl.num_q_heads * pairs
+    # decode on one thread: the first sequence
+    t0 = time.perf_counter()
+    reps1 = 0
+    while time.perf_counter() - t0 < 2.0:
+        orc.workload(dec_wl, rows=np.arange(1, dtype=np.int64), nthreads=1)
+        reps1 += 1
+    dec1_s = (time.perf_counter() - t0) / reps1
+    dec1_bytes = int(dec_wl.seqlens_k[0]) * dec_wl.num_kv_heads * dec_wl.head_dim * 2 * 2
     return dict(
         value=dec_bytes / dec_s / 1e9, unit="GB/s", cores=threads, kind="oracle",
         sample=f"decode: {nseq} of {dec_wl.batch} sequences x 64 heads x 4096 keys "
                f"({dec_bytes} B of K/V), {reps} run(s), {dec_s:.3f} s each",
+        cpu_model=_cpu_model(),
+        decode_one_thread=dict(value=dec1_bytes / dec1_s / 1e9, unit="GB/s", cores=1,
+                               sample=f"decode: 1 sequence x 64 heads x 4096 keys, {reps1} run(s)"),
         prefill=dict(value=pre_flops / pre_s / 1e12, unit="TFLOP/s",
                      sample=f"prefill: {rows.size} query rows (last 16 of each sequence) x 64 heads, "
-                            f"{pre_s:.3f} s"))
+                            f"{pre_s:.3f} s"),
+        router=_cpu_router(), qkv_epilogue=_cpu_epilogue())
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_router():
+    """The router oracle (numpy, fp64) on the first 65536 tokens of the router workload."""
+    from oracle.router import topk_softmax as ref
+    from gqa_attention_head_amd import workloads as W
+    t, e, k = 1 << 16, ROUTER["experts"], ROUTER["k"]
+    _, vals = W.router_logits(12, t, e)
+    t0 = time.perf_counter()
+    ref(vals, k)
+    sec = time.perf_counter() - t0
+    nbytes = t * e * 2 + t * k * 6
+    return dict(value=nbytes / sec / 1e9, unit="GB/s",
+                sample=f"router: {t} tokens x {e} experts, top-{k}, {sec:.3f} s")
+
+
+def _cpu_epilogue():
+    """The epilogue oracle (numpy, fp64) on 1024 tokens of the epilogue workload."""
+    from oracle.rope import qkv_bias_rope as ref
+    from gqa_attention_head_amd import workloads as W
+    t, hq, hkv = 1024, EPILOGUE["hq"], EPILOGUE["hkv"]
+    _, qkv32, _, b32, pos, table = W.qkv_epilogue_inputs(13, t, hq, hkv, 64, EPILOGUE["max_pos"])
+    t0 = time.perf_counter()
+    ref(qkv32, b32, pos, table, hq, hkv, 64)
+    sec = time.perf_counter() - t0
+    nbytes = 2 * t * (hq + 2 * hkv) * 64 * 2
+    return dict(value=nbytes / sec / 1e9, unit="GB/s",
+                sample=f"epilogue: {t} tokens x {hq + 2 * hkv} heads, {sec:.3f} s")
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_decode_b32_kv4096_prefill_b4_s4096.md")
@@ -422,6 +513,8 @@ def main(argv=None):
                    "kv_chunk": dec["chunk"], "num_chunks": dec["num_chunks"],
                    "kv_copies_rotated": KV_COPIES, "parallelism": "single-gpu"},
         "hbm_frac": round(dec["gbs"] / HBM_PEAK_GBS, 4),
+        "step_ms_p10_p50_p90": [round(x, 5) for x in dec["step_ms_p10_p50_p90"]],
+        "context_hbm_torch": context_hbm(),
         "graph_replay": {"ms_per_step": round(dec["graph_ms_per_step"], 5),
                          "value": round(dec["kv_bytes"] / (dec["graph_ms_per_step"] * 1e-3) / 1e9, 2),
                          "unit": "GB/s"},
@@ -436,6 +529,7 @@ def main(argv=None):
         line["prefill"] = {
             "workload": pre["workload"], "value": round(pre["tflops"], 2), "unit": "TFLOP/s",
             "ms": round(pre["ms_mean"], 4), "flops": pre["flops"],
+            "ms_p10_p50_p90": [round(x, 4) for x in pre["ms_p10_p50_p90"]],
             "roofline": {"kernel": "prefill_mfma<8, false>", "bound": "mfma",
                          "achieved": round(pre["tflops"], 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(pre["tflops"] / BF16_PEAK_TFLOPS, 4),

@@ -36,6 +36,20 @@ METRIC = "decode KV GB/s (% HBM peak); prefill TFLOP/s (% bf16 MFMA peak)"
 KV_COPIES = 5                  # 5 x 268 MB rotated
 
 
+def warm_up(fn, launches: int, min_ms: float = 0.0):
+    """Untimed launches: at least `launches`, and more until `min_ms` of wall time has
+    passed (the clocks settle over some tens of milliseconds after the load changes)."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < launches or (time.perf_counter() - t0) * 1e3 < min_ms:
+        fn(i)
+        i += 1
+        if i % 20 == 0:
+            _sync()
+    _sync()
+    return i
+
+
 def _sync():
     import torch
     if torch.distributed.is_available() and torch.distributed.is_initialized():
@@ -146,11 +160,9 @@ def bench_prefill(steps: int, warmup: int):
     def step():
         sa.prefill(q, k, v, sinks, cu_q, cu_k, lq, lq, wl.sm_scale, causal=True, out=out, lse=lse)
 
-    # The clock needs some tens of milliseconds of load to settle after idle: the
-    # warm-up runs at least 50 launches (about 30 ms) before the timed run.
-    for _ in range(max(warmup, 50)):
-        step()
-    _sync()
+    # The clocks need some tens of milliseconds of load to settle after idle or a
+    # change of load: at least 50 launches and 60 ms of warm-up before the timed run.
+    warm_up(lambda i: step(), max(warmup, 50), 60.0)
     # back-to-back launches between one event pair on the launch stream
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     ev[0].record()
@@ -285,9 +297,7 @@ def bench_router(steps: int, warmup: int):
     lgs = [lg0] + [lg0.clone() for _ in range(ROUTER["copies"] - 1)]
     idx = torch.empty(t, k, device=dev, dtype=torch.int32)
     w = torch.empty(t, k, device=dev, dtype=torch.bfloat16)
-    for i in range(warmup):
-        sa.topk_softmax(lgs[i % len(lgs)], k, indices=idx, weights=w)
-    _sync()
+    warm_up(lambda i: sa.topk_softmax(lgs[i % len(lgs)], k, indices=idx, weights=w), warmup, 60.0)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(steps):
@@ -324,9 +334,7 @@ def bench_epilogue(steps: int, warmup: int):
     k = torch.empty(t, hkv, 64, device=dev, dtype=torch.bfloat16)
     v = torch.empty(t, hkv, 64, device=dev, dtype=torch.bfloat16)
     call = lambda i: sa.qkv_bias_rope(xs[i % len(xs)], bias, pos_d, tab, hq, hkv, q=q, k=k, v=v)
-    for i in range(warmup):
-        call(i)
-    _sync()
+    warm_up(call, warmup, 60.0)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(steps):

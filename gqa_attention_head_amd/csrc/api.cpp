@@ -336,8 +336,9 @@ sa_status_t qkv_bias_rope(const void* qkv, const void* bias, const int32_t* posi
     if (table_rows < 1) return fail(SA_EINVAL, "table_rows must be >= 1");
     const int64_t heads = (int64_t)num_q_heads + 2 * (int64_t)num_kv_heads;
     sa_status_t s;
-    // one thread per quarter head: num_tokens * heads * 4 work-items, below 2^32
-    if (num_tokens > (int64_t)0xFFFFFFFFLL / (heads * 4))
+    // eight 16-byte pieces per head, two per thread: num_tokens * heads * 4 work-items
+    // (rounded up to whole blocks of 256), below 2^32
+    if (num_tokens > ((int64_t)0xFFFFFFFFLL - 512) / (heads * 4))
         return fail(SA_EINVAL, "qkv_bias_rope: num_tokens * heads * 4 exceeds the 2^32 work-item grid limit");
     if (num_tokens == 0) return ok();  // nothing to read or write: pointers may be null
     if (!qkv || !bias || !positions || !cos_sin || !q || !k || !v)

@@ -8,8 +8,13 @@
 // (rotate-halves pairing: element i with element i + 32) and writes q, k and v
 // in the [token, head, 64] layouts the attention entry points read.
 //
-// Thread (token t, head hh, quarter j): elements 8j .. 8j+7 and 32+8j .. 32+8j+7
-// of head hh, so four threads cover a head and a wave sixteen heads.
+// Layout: the projection output is streamed as 16-byte pieces, eight per head,
+// piece p of a head holding elements 8p .. 8p+7 in lane p of an aligned group of
+// eight lanes, so every load and store instruction of a wave covers whole
+// 128-byte head rows (1 KB contiguous).  The rotation partner of piece p < 4 is
+// piece p + 4, one lane-xor-4 swizzle away.  Each thread handles two pieces 256
+// apart, and both loads are issued before either is used.  The projection output
+// and q/k/v are touched once (nontemporal); bias and table rows stay cached.
 #include "common.h"
 #include "kernels.h"
 
@@ -18,6 +23,7 @@ namespace sa {
 namespace {
 
 constexpr int kD = 64;
+constexpr int kItems = 2;  // pieces per thread
 
 __device__ __forceinline__ void unpack8(u32x4 w, float* x) {
 #pragma unroll
@@ -41,50 +47,60 @@ __global__ __launch_bounds__(256) void qkv_rope_kernel(
     int64_t num_tokens, int hq, int hkv, int rows, uint16_t* __restrict__ q,
     uint16_t* __restrict__ k, uint16_t* __restrict__ v) {
     const int heads = hq + 2 * hkv;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int j = (int)(gid % 4);
-    const int64_t rest = gid / 4;
-    const int hh = (int)(rest % heads);
-    const int64_t t = rest / heads;
-    if (t >= num_tokens) return;
-
-    const uint16_t* src = qkv + (t * heads + hh) * kD;
-    const uint16_t* bs = bias + (int64_t)hh * kD;
-    float lo[8], hi[8], blo[8], bhi[8];
-    unpack8(*reinterpret_cast<const u32x4*>(src + 8 * j), lo);
-    unpack8(*reinterpret_cast<const u32x4*>(src + 32 + 8 * j), hi);
-    unpack8(*reinterpret_cast<const u32x4*>(bs + 8 * j), blo);
-    unpack8(*reinterpret_cast<const u32x4*>(bs + 32 + 8 * j), bhi);
+    const int64_t total = num_tokens * heads * 8;  // 16-byte pieces
+    const int64_t base = (int64_t)blockIdx.x * 256 * kItems + threadIdx.x;
+    u32x4 raw[kItems];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        lo[e] += blo[e];
-        hi[e] += bhi[e];
+    for (int u = 0; u < kItems; ++u) {
+        const int64_t gid = base + u * 256;
+        raw[u] = u32x4{0u, 0u, 0u, 0u};
+        if (gid < total) raw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qkv) + gid);
     }
-    if (hh < hq + hkv) {  // query or key head: rotate
-        const int p = min(max(positions[t], 0), rows - 1);
-        const float* row = cos_sin + (int64_t)p * kD;
-        const f32x4 c0 = *reinterpret_cast<const f32x4*>(row + 8 * j);
-        const f32x4 c1 = *reinterpret_cast<const f32x4*>(row + 8 * j + 4);
-        const f32x4 s0 = *reinterpret_cast<const f32x4*>(row + 32 + 8 * j);
-        const f32x4 s1 = *reinterpret_cast<const f32x4*>(row + 32 + 8 * j + 4);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float c = (e < 4) ? c0[e] : c1[e - 4];
-            const float s = (e < 4) ? s0[e] : s1[e - 4];
-            const float a = lo[e], b = hi[e];
-            lo[e] = __builtin_fmaf(a, c, -b * s);
-            hi[e] = __builtin_fmaf(b, c, a * s);
+    for (int u = 0; u < kItems; ++u) {
+        const int64_t gid = base + u * 256;
+        const int piece = (int)(gid % 8);
+        const int64_t rest = gid / 8;
+        const int hh = (int)(rest % heads);
+        const int64_t t = rest / heads;
+        const bool live = gid < total;  // uniform over each group of eight lanes
+        float x[8], b[8];
+        unpack8(raw[u], x);
+        unpack8(*reinterpret_cast<const u32x4*>(bias + hh * kD + 8 * piece), b);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] += b[e];
+        // every lane takes part in the exchange: partner = lane ^ 4 (same head)
+        float pr[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            pr[e] = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x[e]), 0x101F));
+        if (live && hh < hq + hkv) {  // query or key head: rotate
+            const int p = min(max(positions[t], 0), rows - 1);
+            const int i = piece % 4;
+            const float* row = cos_sin + (int64_t)p * kD;
+            const f32x4 c0 = *reinterpret_cast<const f32x4*>(row + 8 * i);
+            const f32x4 c1 = *reinterpret_cast<const f32x4*>(row + 8 * i + 4);
+            const f32x4 s0 = *reinterpret_cast<const f32x4*>(row + 32 + 8 * i);
+            const f32x4 s1 = *reinterpret_cast<const f32x4*>(row + 32 + 8 * i + 4);
+            // low half: x c - partner s; high half: x c + partner s
+            const float sign = piece < 4 ? -1.0f : 1.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float c = (e < 4) ? c0[e] : c1[e - 4];
+                const float s = (e < 4) ? s0[e] : s1[e - 4];
+                x[e] = __builtin_fmaf(x[e], c, sign * (pr[e] * s));
+            }
         }
+        if (!live) continue;
+        uint16_t* dst;
+        if (hh < hq)
+            dst = q + (t * hq + hh) * kD;
+        else if (hh < hq + hkv)
+            dst = k + (t * hkv + (hh - hq)) * kD;
+        else
+            dst = v + (t * hkv + (hh - hq - hkv)) * kD;
+        __builtin_nontemporal_store(pack8(x), reinterpret_cast<u32x4*>(dst + 8 * piece));
     }
-    uint16_t* dst;
-    if (hh < hq)
-        dst = q + (t * hq + hh) * kD;
-    else if (hh < hq + hkv)
-        dst = k + (t * hkv + (hh - hq)) * kD;
-    else
-        dst = v + (t * hkv + (hh - hq - hkv)) * kD;
-    *reinterpret_cast<u32x4*>(dst + 8 * j) = pack8(lo);
-    *reinterpret_cast<u32x4*>(dst + 32 + 8 * j) = pack8(hi);
 }
 
 }  // namespace
@@ -92,8 +108,8 @@ __global__ __launch_bounds__(256) void qkv_rope_kernel(
 hipError_t launch_qkv_rope(const void* qkv, const void* bias, const int32_t* positions,
                            const float* cos_sin, int64_t num_tokens, int hq, int hkv, int rows,
                            void* q, void* k, void* v, hipStream_t stream) {
-    const int64_t threads = num_tokens * (hq + 2 * hkv) * 4;
-    const int64_t blocks = (threads + 255) / 256;
+    const int64_t pieces = num_tokens * (hq + 2 * hkv) * 8;
+    const int64_t blocks = (pieces + 256 * kItems - 1) / (256 * kItems);
     hipLaunchKernelGGL(qkv_rope_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(qkv), static_cast<const uint16_t*>(bias),
                        positions, cos_sin, num_tokens, hq, hkv, rows, static_cast<uint16_t*>(q),

@@ -440,3 +440,34 @@ def test_prefill_split_matches_unsplit():
     full_lse = full_lse.cpu().numpy().astype(np.float64)
     assert np.abs(out - full).max() <= H.BF16_MAX_ABS
     assert np.abs(lse - full_lse).max() <= 1e-4
+
+
+# ---------------------------------------------------------------- long inputs
+
+def test_long_single_sequence_prefill_sampled(orc):
+    """One 32768-token causal sequence (64/8 heads): the longest rows of the path's
+    prefill kernel, checked on sampled rows including the last ones."""
+    wl = W.make_workload("long_prefill", dtype="bf16", kind="prefill", seqlens_q=[32768],
+                         seqlens_k=[32768], num_q_heads=64, num_kv_heads=8, head_dim=64, seed=71,
+                         causal=True)
+    dev = H.Device(wl)
+    out, lse = H.run_prefill(dev)
+    rows = np.array([0, 63, 64, 4095, 16384, 32766, 32767], dtype=np.int64)
+    ref, ref_lse = orc.workload(wl, rows=rows, nthreads=NTHREADS)
+    H.assert_close(out[rows], ref, bf16=True)
+    H.assert_lse_close(lse[rows], ref_lse, bf16=True)
+    assert np.all(np.isfinite(out))
+
+
+def test_long_kv_split_prefill_bench_shape(orc):
+    """The benchmark's chunked prefill: 256 new tokens over 131072 keys (64/8 heads),
+    16384-key chunks, split pass then row merge; sampled rows against the oracle."""
+    wl = W.make_workload("long_kv", dtype="bf16", kind="prefill", seqlens_q=[256],
+                         seqlens_k=[131072], num_q_heads=64, num_kv_heads=8, head_dim=64,
+                         seed=72, causal=True)
+    dev = H.Device(wl)
+    _, _, _, out, lse = run_prefill_split(dev, 16384)
+    rows = np.array([0, 1, 31, 32, 128, 254, 255], dtype=np.int64)
+    ref, ref_lse = orc.workload(wl, rows=rows, nthreads=NTHREADS)
+    H.assert_close(out[rows], ref, bf16=True)
+    H.assert_lse_close(lse[rows], ref_lse, bf16=True)

@@ -22,7 +22,8 @@ SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_ELAUNCH = 0, 1, 2, 3
 SA_FP32, SA_BF16 = 0, 1
 EXPORTS = ("sink_attn_prefill", "sink_attn_decode_split", "sink_attn_merge",
            "sink_attn_decode", "sink_attn_prefill_split", "sink_attn_merge_rows",
-           "sink_attn_last_error", "moe_topk_softmax", "qkv_bias_rope")
+           "sink_attn_last_error", "moe_topk_softmax", "qkv_bias_rope",
+           "sink_attn_prefill_state")
 
 
 class SinkAttnError(RuntimeError):
@@ -68,6 +69,9 @@ def load_library():
     lib.sink_attn_merge_rows.argtypes = [ctypes.c_int, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.moe_topk_softmax.restype = ctypes.c_int
     lib.moe_topk_softmax.argtypes = [vp, ctypes.c_int64, i32, i32, vp, vp, vp]
+    lib.sink_attn_prefill_state.restype = ctypes.c_int
+    lib.sink_attn_prefill_state.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i32, i32,
+                                            i32, i32, i32, f32, i32, i32, i32, i32, vp, vp, vp, vp]
     lib.qkv_bias_rope.restype = ctypes.c_int
     lib.qkv_bias_rope.argtypes = [vp, vp, vp, vp, ctypes.c_int64, i32, i32, i32, i32, vp, vp, vp,
                                   vp]
@@ -175,6 +179,39 @@ def prefill_split(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_
         _ptr(cu_seqlens_k), cu_seqlens_q.numel() - 1, q.shape[1], k.shape[1], q.shape[2],
         int(max_seqlen_q), int(max_seqlen_k), int(kv_chunk_size), int(max_num_chunks),
         float(sm_scale), int(bool(causal)), _ptr(pm), _ptr(pd), _ptr(pa), _stream(stream)))
+    return pm, pd, pa
+
+
+def prefill_state(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                  sm_scale, causal=True, include_sink=True, slot=0, num_slots=None,
+                  partials=None, stream=None):
+    """Per-row attention state over the keys of this call, into slot ``slot`` of the
+    state buffers (``sink_attn_prefill_state``), for cascade attention; the buffers
+    (part_m, part_d, part_acc) are [total_q, Hq, num_slots(, D)] and are returned."""
+    torch = _torch()
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name, q.dtype)
+    _dev(sinks, "sinks", torch.float32)
+    _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3 or k.shape != v.shape:
+        raise ValueError("q must be [total_q, Hq, D]; k and v [total_k, Hkv, D]")
+    if partials is None:
+        if num_slots is None:
+            raise ValueError("give num_slots or partials")
+        partials = partial_buffers(q.shape[0], q.shape[1], num_slots, q.shape[2], q.device)
+    pm, pd, pa = partials
+    for name, t in (("part_m", pm), ("part_d", pd), ("part_acc", pa)):
+        _dev(t, name, torch.float32)
+    if pm.dim() != 3 or tuple(pm.shape[:2]) != (q.shape[0], q.shape[1]):
+        raise ValueError("part_m must be [total_q, Hq, num_slots]")
+    _check(lib.sink_attn_prefill_state(
+        _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(cu_seqlens_q),
+        _ptr(cu_seqlens_k), cu_seqlens_q.numel() - 1, q.shape[1], k.shape[1], q.shape[2],
+        int(max_seqlen_q), int(max_seqlen_k), float(sm_scale), int(bool(causal)),
+        int(bool(include_sink)), int(slot), pm.shape[2], _ptr(pm), _ptr(pd), _ptr(pa),
+        _stream(stream)))
     return pm, pd, pa
 
 

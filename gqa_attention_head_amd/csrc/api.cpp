@@ -167,17 +167,67 @@ sa_status_t sink_attn_prefill_split(sa_dtype_t dtype, const void* q, const void*
     if ((s = check_device()) != SA_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e;
+    const sa::StateSlots ss{kv_chunk_size, max_num_chunks, max_num_chunks, 0, 1};
     if (mfma)
         e = sa::launch_mfma_prefill_split(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, batch,
-                                          num_q_heads, num_kv_heads, max_seqlen_q, kv_chunk_size,
-                                          max_num_chunks, sm_scale, causal, nullptr, nullptr,
-                                          part_m, part_d, part_acc, st);
+                                          num_q_heads, num_kv_heads, max_seqlen_q, ss, sm_scale,
+                                          causal, part_m, part_d, part_acc, st);
     else
         e = sa::launch_generic_prefill_split(dtype == SA_BF16, q, k, v, sinks, cu_seqlens_q,
                                              cu_seqlens_k, batch, num_q_heads, num_kv_heads,
-                                             max_seqlen_q, kv_chunk_size, max_num_chunks, sm_scale,
-                                             causal, part_m, part_d, part_acc, st);
+                                             max_seqlen_q, ss, sm_scale, causal, part_m, part_d,
+                                             part_acc, st);
     return finish_launch(e, st, "sink_attn_prefill_split");
+}
+
+sa_status_t sink_attn_prefill_state(sa_dtype_t dtype, const void* q, const void* k, const void* v,
+                                    const float* sinks, const int32_t* cu_seqlens_q,
+                                    const int32_t* cu_seqlens_k, int32_t batch,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t max_seqlen_q, int32_t max_seqlen_k, float sm_scale,
+                                    int32_t causal, int32_t include_sink, int32_t slot,
+                                    int32_t num_slots, float* part_m, float* part_d,
+                                    float* part_acc, void* stream) {
+    sa_status_t s;
+    if ((s = check_dtype(dtype)) != SA_OK) return s;
+    if (!q || !k || !v || !sinks || !cu_seqlens_q || !cu_seqlens_k || !part_m || !part_d ||
+        !part_acc)
+        return fail(SA_EINVAL, "sink_attn_prefill_state: null pointer argument");
+    if ((s = check_heads(batch, num_q_heads, num_kv_heads, head_dim)) != SA_OK) return s;
+    if (max_seqlen_q < 0 || max_seqlen_k < 0)
+        return fail(SA_EINVAL, "max_seqlen_q/max_seqlen_k must be >= 0");
+    if (causal != 0 && causal != 1) return fail(SA_EINVAL, "causal must be 0 or 1");
+    if (include_sink != 0 && include_sink != 1) return fail(SA_EINVAL, "include_sink must be 0 or 1");
+    if (num_slots < 1) return fail(SA_EINVAL, "num_slots must be >= 1, got %d", num_slots);
+    if (slot < 0 || slot >= num_slots)
+        return fail(SA_EINVAL, "slot %d is outside [0, num_slots = %d)", slot, num_slots);
+    if (!(std::isfinite(sm_scale) && sm_scale > 0.0f))
+        return fail(SA_EINVAL, "sm_scale must be finite and > 0");
+    const int group = num_q_heads / num_kv_heads;
+    const bool mfma = dtype == SA_BF16 && sa::mfma_prefill_supported(group);
+    if (mfma) {
+        if ((s = check_grid((int64_t)batch * num_kv_heads * ((max_seqlen_q + 31) / 32), 64 * group,
+                            "sink_attn_prefill_state")) != SA_OK)
+            return s;
+    } else if ((s = check_grid(max_seqlen_q, 64, "sink_attn_prefill_state")) != SA_OK) {
+        return s;
+    }
+    if (max_seqlen_q == 0) return ok();
+    if ((s = check_device()) != SA_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // one chunk starting at key 0 that no sequence outgrows
+    const sa::StateSlots ss{0x7fffffff, 1, num_slots, slot, include_sink};
+    hipError_t e;
+    if (mfma)
+        e = sa::launch_mfma_prefill_split(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, batch,
+                                          num_q_heads, num_kv_heads, max_seqlen_q, ss, sm_scale,
+                                          causal, part_m, part_d, part_acc, st);
+    else
+        e = sa::launch_generic_prefill_split(dtype == SA_BF16, q, k, v, sinks, cu_seqlens_q,
+                                             cu_seqlens_k, batch, num_q_heads, num_kv_heads,
+                                             max_seqlen_q, ss, sm_scale, causal, part_m, part_d,
+                                             part_acc, st);
+    return finish_launch(e, st, "sink_attn_prefill_state");
 }
 
 sa_status_t sink_attn_merge_rows(sa_dtype_t out_dtype, const float* part_m, const float* part_d,

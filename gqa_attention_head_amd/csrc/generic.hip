@@ -38,13 +38,15 @@ __device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) { return f32_to_
 enum Mode { kRows, kDecodeSplit, kRowsSplit };
 
 // grid.x: block of query rows (kRows, kRowsSplit) or key chunk (kDecodeSplit);
-// grid.y: KV head; grid.z: sequence (kRowsSplit: sequence * max_chunks + chunk).
+// grid.y: KV head; grid.z: sequence (kRowsSplit: sequence * ss.n_chunks + chunk).
+// Split modes write chunk c's state of row r to slot r * ss.stride + ss.slot0 + c;
+// the sink enters chunk 0 when ss.sink is set.
 template <typename T, Mode kMode>
 __global__ __launch_bounds__(64) void rows_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ sinks, const int32_t* __restrict__ cu_q,
-    const int32_t* __restrict__ cu_k, int hq, int hkv, float scale_log2, int causal, int chunk,
-    int max_chunks, T* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_m,
+    const int32_t* __restrict__ cu_k, int hq, int hkv, float scale_log2, int causal,
+    StateSlots ss, T* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_m,
     float* __restrict__ part_d, float* __restrict__ part_acc) {
     __shared__ float ks[kTileKeys][kD];
     __shared__ float vs[kTileKeys][kD];
@@ -54,7 +56,7 @@ __global__ __launch_bounds__(64) void rows_kernel(
     const int lane = threadIdx.x;
     constexpr bool kSplit = kMode != kRows;
     const int g = blockIdx.y;
-    const int b = (kMode == kRowsSplit) ? blockIdx.z / max_chunks : blockIdx.z;
+    const int b = (kMode == kRowsSplit) ? blockIdx.z / ss.n_chunks : blockIdx.z;
     const int r_local = lane / group, hh = lane % group;
     const int h = g * group + hh;
 
@@ -66,11 +68,11 @@ __global__ __launch_bounds__(64) void rows_kernel(
         lq = 1;
         row = r_local;  // one query per sequence: only lanes with r_local == 0 are active
         const int c = blockIdx.x;
-        const int nch = max(1, ceil_div(lk, chunk));
+        const int nch = max(1, ceil_div(lk, ss.chunk));
         if (c >= nch) return;
-        key_lo = c * chunk;
-        key_hi = min(key_lo + chunk, lk);
-        first_block = (c == 0);
+        key_lo = c * ss.chunk;
+        key_hi = min(key_lo + ss.chunk, lk);
+        first_block = (c == 0 && ss.sink != 0);
     } else {
         const int q0 = cu_q[b];
         lq = cu_q[b + 1] - q0;
@@ -82,10 +84,10 @@ __global__ __launch_bounds__(64) void rows_kernel(
         key_hi = causal ? max(0, min(lk, lk - lq + last + 1)) : lk;
         first_block = true;
         if (kMode == kRowsSplit) {  // this launch index's chunk of the keys
-            const int c = blockIdx.z % max_chunks;
-            key_lo = c * chunk;
-            key_hi = min(key_hi, key_lo + chunk);
-            first_block = (c == 0);
+            const int c = blockIdx.z % ss.n_chunks;
+            key_lo = c * ss.chunk;
+            key_hi = min(key_hi, key_lo + ss.chunk);
+            first_block = (c == 0 && ss.sink != 0);
         }
     }
     const bool active = (r_local < rows_per_wave) && (row < lq);
@@ -147,9 +149,9 @@ __global__ __launch_bounds__(64) void rows_kernel(
     if (!active) return;
 
     if (kSplit) {
-        const int c = (kMode == kDecodeSplit) ? blockIdx.x : blockIdx.z % max_chunks;
+        const int c = (kMode == kDecodeSplit) ? blockIdx.x : blockIdx.z % ss.n_chunks;
         const int64_t srow = (kMode == kDecodeSplit) ? (int64_t)b : (int64_t)cu_q[b] + row;
-        const int64_t slot = (srow * hq + h) * max_chunks + c;
+        const int64_t slot = (srow * hq + h) * ss.stride + ss.slot0 + c;
         part_m[slot] = (m == kNegInf) ? kNegInf : m * kLn2;
         part_d[slot] = dsum;
         float* pa = part_acc + slot * kD;
@@ -184,12 +186,12 @@ hipError_t launch_generic_prefill(bool bf16, const void* q, const void* k, const
     if (bf16)
         hipLaunchKernelGGL((rows_kernel<uint16_t, kRows>), grid, dim3(64), 0, stream,
                            (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, sinks, cu_q,
-                           cu_k, hq, hkv, sl, causal, 0, 0, (uint16_t*)out, lse, nullptr, nullptr,
-                           nullptr);
+                           cu_k, hq, hkv, sl, causal, StateSlots{0, 1, 1, 0, 1}, (uint16_t*)out,
+                           lse, nullptr, nullptr, nullptr);
     else
         hipLaunchKernelGGL((rows_kernel<float, kRows>), grid, dim3(64), 0, stream, (const float*)q,
                            (const float*)k, (const float*)v, sinks, cu_q, cu_k, hq, hkv, sl, causal,
-                           0, 0, (float*)out, lse, nullptr, nullptr, nullptr);
+                           StateSlots{0, 1, 1, 0, 1}, (float*)out, lse, nullptr, nullptr, nullptr);
     return hipGetLastError();
 }
 
@@ -200,38 +202,38 @@ hipError_t launch_generic_decode_split(bool bf16, const void* q, const void* k, 
                                        hipStream_t stream) {
     dim3 grid(max_chunks, hkv, batch);
     const float sl = sm_scale * kLog2e;
+    const StateSlots ss{chunk, max_chunks, max_chunks, 0, 1};
     if (bf16)
         hipLaunchKernelGGL((rows_kernel<uint16_t, kDecodeSplit>), grid, dim3(64), 0, stream,
                            (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, sinks,
-                           nullptr, cu_k, hq, hkv, sl, 0, chunk, max_chunks, nullptr, nullptr,
-                           part_m, part_d, part_acc);
+                           nullptr, cu_k, hq, hkv, sl, 0, ss, nullptr, nullptr, part_m, part_d,
+                           part_acc);
     else
         hipLaunchKernelGGL((rows_kernel<float, kDecodeSplit>), grid, dim3(64), 0, stream, (const float*)q,
                            (const float*)k, (const float*)v, sinks, nullptr, cu_k, hq, hkv, sl, 0,
-                           chunk, max_chunks, nullptr, nullptr, part_m, part_d, part_acc);
+                           ss, nullptr, nullptr, part_m, part_d, part_acc);
     return hipGetLastError();
 }
 
 hipError_t launch_generic_prefill_split(bool bf16, const void* q, const void* k, const void* v,
                                         const float* sinks, const int32_t* cu_q,
                                         const int32_t* cu_k, int batch, int hq, int hkv,
-                                        int max_lq, int chunk, int max_chunks, float sm_scale,
+                                        int max_lq, const StateSlots& ss, float sm_scale,
                                         int causal, float* part_m, float* part_d,
                                         float* part_acc, hipStream_t stream) {
     const int group = hq / hkv;
     const int rows_per_wave = 64 / group;
-    dim3 grid(ceil_div(max_lq, rows_per_wave), hkv, batch * max_chunks);
+    dim3 grid(ceil_div(max_lq, rows_per_wave), hkv, batch * ss.n_chunks);
     const float sl = sm_scale * kLog2e;
     if (bf16)
         hipLaunchKernelGGL((rows_kernel<uint16_t, kRowsSplit>), grid, dim3(64), 0, stream,
                            (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, sinks, cu_q,
-                           cu_k, hq, hkv, sl, causal, chunk, max_chunks, nullptr, nullptr, part_m,
-                           part_d, part_acc);
+                           cu_k, hq, hkv, sl, causal, ss, nullptr, nullptr, part_m, part_d,
+                           part_acc);
     else
         hipLaunchKernelGGL((rows_kernel<float, kRowsSplit>), grid, dim3(64), 0, stream,
                            (const float*)q, (const float*)k, (const float*)v, sinks, cu_q, cu_k, hq,
-                           hkv, sl, causal, chunk, max_chunks, nullptr, nullptr, part_m, part_d,
-                           part_acc);
+                           hkv, sl, causal, ss, nullptr, nullptr, part_m, part_d, part_acc);
     return hipGetLastError();
 }
 

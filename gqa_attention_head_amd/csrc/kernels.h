@@ -6,6 +6,20 @@
 
 namespace sa {
 
+// Where the split (state-writing) prefill kernels put their (m, d, acc) states:
+// the keys of each sequence are cut into n_chunks chunks of `chunk` keys (one
+// chunk per launch index); chunk c of query row r goes to slot r * stride + slot0
+// + c of the [rows, Hq, stride] state buffers.  The head's sink enters chunk 0's
+// state when `sink` is nonzero and no state otherwise.
+struct StateSlots {
+    int chunk;
+    int n_chunks;
+    int stride;
+    int slot0;
+    int sink;
+};
+
+
 // Vector-ALU kernel, float32 arithmetic; any group size G = hq / hkv <= 64, head_dim 64.
 hipError_t launch_generic_prefill(bool bf16, const void* q, const void* k, const void* v,
                                   const float* sinks, const int32_t* cu_q, const int32_t* cu_k,
@@ -14,7 +28,7 @@ hipError_t launch_generic_prefill(bool bf16, const void* q, const void* k, const
 hipError_t launch_generic_prefill_split(bool bf16, const void* q, const void* k, const void* v,
                                         const float* sinks, const int32_t* cu_q,
                                         const int32_t* cu_k, int batch, int hq, int hkv,
-                                        int max_lq, int chunk, int max_chunks, float sm_scale,
+                                        int max_lq, const StateSlots& ss, float sm_scale,
                                         int causal, float* part_m, float* part_d,
                                         float* part_acc, hipStream_t stream);
 hipError_t launch_generic_decode_split(bool bf16, const void* q, const void* k, const void* v,
@@ -34,10 +48,9 @@ bool mfma_prefill_supported(int group);
 // Chunk states of every (query row, head, key chunk) instead of the output.
 hipError_t launch_mfma_prefill_split(const void* q, const void* k, const void* v,
                                      const float* sinks, const int32_t* cu_q, const int32_t* cu_k,
-                                     int batch, int hq, int hkv, int max_lq, int chunk,
-                                     int max_chunks, float sm_scale, int causal, void* out,
-                                     float* lse, float* part_m, float* part_d, float* part_acc,
-                                     hipStream_t stream);
+                                     int batch, int hq, int hkv, int max_lq, const StateSlots& ss,
+                                     float sm_scale, int causal, float* part_m, float* part_d,
+                                     float* part_acc, hipStream_t stream);
 hipError_t launch_mfma_prefill(const void* q, const void* k, const void* v, const float* sinks,
                                const int32_t* cu_q, const int32_t* cu_k, int batch, int hq,
                                int hkv, int max_lq, float sm_scale, int causal, void* out,

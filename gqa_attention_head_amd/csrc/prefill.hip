@@ -67,18 +67,20 @@ __device__ __forceinline__ float exp_tile(const f32x16 (&s)[2], float scale_log2
     return psum;
 }
 
-// kSplit: the keys of each sequence are cut into chunks of `chunk` keys, one
-// chunk per launch index (the slowest grid dimension), and the kernel writes each
-// row's state after its chunk (m in natural-log units, d, unnormalised acc) to
-// slot (row, head, chunk) instead of the normalised output.  The sink enters
-// chunk 0's state only; a chunk a row cannot see leaves (m = -inf, d = 0, acc = 0).
+// kSplit: the keys of each sequence are cut into ss.n_chunks chunks of ss.chunk
+// keys, one chunk per launch index (the slowest grid dimension), and the kernel
+// writes each row's state after its chunk (m in natural-log units, d, unnormalised
+// acc) to slot (row, head, ss.slot0 + chunk) of buffers with ss.stride slots per
+// (row, head), instead of the normalised output.  The sink enters chunk 0's state
+// only, and only when ss.sink is set; a chunk a row cannot see leaves
+// (m = -inf, d = 0, acc = 0).
 template <int G, bool kSplit>
 __global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4)))
 void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                   const uint16_t* __restrict__ v, const float* __restrict__ sinks,
                   const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int hq,
                   int hkv, int batch, int n_qblocks, float scale_log2, int causal,
-                  uint16_t* __restrict__ out, float* __restrict__ lse, int chunk, int max_chunks,
+                  uint16_t* __restrict__ out, float* __restrict__ lse, StateSlots ss,
                   float* __restrict__ part_m, float* __restrict__ part_d,
                   float* __restrict__ part_acc) {
     constexpr int kThreads = 64 * G;
@@ -120,10 +122,10 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     int kend = causal ? max(0, min(lk, lk - lq + last + 1)) : lk;
     int full_end = causal ? max(0, min(lk, lk - lq + r0 + 1)) : lk;
     // this launch's keys start at k_lo (0 unless split); rows see keys below row_lim
-    const int k_lo = c * chunk;
+    const int k_lo = kSplit ? c * ss.chunk : 0;
     if (kSplit) {
-        kend = min(kend, k_lo + chunk);
-        full_end = min(full_end, k_lo + chunk);
+        kend = min(kend, k_lo + ss.chunk);
+        full_end = min(full_end, k_lo + ss.chunk);
     }
     const int row_lim = min(kend, causal ? lk - lq + row + 1 : lk);
 
@@ -137,8 +139,9 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 
     // Running state (base 2): the maximum starts at the sink (the first and only
     // block of keys holds it) and the scale at 1, split over the two lane halves.
-    float m = (c == 0) ? sinks[h] * kLog2e : kNegInf;
-    float dl = (half == 0 && c == 0) ? 1.0f : 0.0f;
+    const bool with_sink = kSplit ? (c == 0 && ss.sink != 0) : true;
+    float m = with_sink ? sinks[h] * kLog2e : kNegInf;
+    float dl = (half == 0 && with_sink) ? 1.0f : 0.0f;
     f32x16 o[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -256,7 +259,7 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     if (!row_ok) return;
     const int64_t orow = (int64_t)(q0 + row) * hq + h;
     if (kSplit) {
-        const int64_t slot = orow * max_chunks + c;
+        const int64_t slot = orow * ss.stride + ss.slot0 + c;
         float* pa = part_acc + slot * kD;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
@@ -293,23 +296,36 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 template <int G>
 hipError_t launch_g(const void* q, const void* k, const void* v, const float* sinks,
                     const int32_t* cu_q, const int32_t* cu_k, int batch, int hq, int hkv,
-                    int max_lq, float sm_scale, int causal, void* out, float* lse, int chunk,
-                    int max_chunks, float* part_m, float* part_d, float* part_acc,
+                    int max_lq, float sm_scale, int causal, void* out, float* lse,
+                    const StateSlots& ss, float* part_m, float* part_d, float* part_acc,
                     hipStream_t stream) {
     const int n_qblocks = ceil_div(max_lq, kBQ);
     const bool split = part_m != nullptr;
-    const int64_t blocks = (int64_t)batch * hkv * n_qblocks * (split ? max_chunks : 1);
+    const int64_t blocks = (int64_t)batch * hkv * n_qblocks * (split ? ss.n_chunks : 1);
     if (split)
         hipLaunchKernelGGL((prefill_mfma<G, true>), dim3((unsigned)blocks), dim3(64 * G), 0,
                            stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                            sinks, cu_q, cu_k, hq, hkv, batch, n_qblocks, sm_scale * kLog2e, causal,
-                           nullptr, nullptr, chunk, max_chunks, part_m, part_d, part_acc);
+                           nullptr, nullptr, ss, part_m, part_d, part_acc);
     else
         hipLaunchKernelGGL((prefill_mfma<G, false>), dim3((unsigned)blocks), dim3(64 * G), 0,
                            stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                            sinks, cu_q, cu_k, hq, hkv, batch, n_qblocks, sm_scale * kLog2e, causal,
-                           (uint16_t*)out, lse, 0, 1, nullptr, nullptr, nullptr);
+                           (uint16_t*)out, lse, ss, nullptr, nullptr, nullptr);
     return hipGetLastError();
+}
+
+hipError_t dispatch(const void* q, const void* k, const void* v, const float* sinks,
+                    const int32_t* cu_q, const int32_t* cu_k, int batch, int hq, int hkv,
+                    int max_lq, float sm_scale, int causal, void* out, float* lse,
+                    const StateSlots& ss, float* part_m, float* part_d, float* part_acc,
+                    hipStream_t stream) {
+    switch (hq / hkv) {
+#define SA_CASE(GG) case GG: return launch_g<GG>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, ss, part_m, part_d, part_acc, stream);
+        SA_CASE(1) SA_CASE(2) SA_CASE(4) SA_CASE(8) SA_CASE(16)
+#undef SA_CASE
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -322,24 +338,18 @@ hipError_t launch_mfma_prefill(const void* q, const void* k, const void* v, cons
                                const int32_t* cu_q, const int32_t* cu_k, int batch, int hq,
                                int hkv, int max_lq, float sm_scale, int causal, void* out,
                                float* lse, hipStream_t stream) {
-    return launch_mfma_prefill_split(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, 0, 1,
-                                     sm_scale, causal, out, lse, nullptr, nullptr, nullptr, stream);
+    const StateSlots whole{0, 1, 1, 0, 1};  // one block of keys, sink included
+    return dispatch(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out,
+                    lse, whole, nullptr, nullptr, nullptr, stream);
 }
 
 hipError_t launch_mfma_prefill_split(const void* q, const void* k, const void* v,
                                      const float* sinks, const int32_t* cu_q, const int32_t* cu_k,
-                                     int batch, int hq, int hkv, int max_lq, int chunk,
-                                     int max_chunks, float sm_scale, int causal, void* out,
-                                     float* lse, float* part_m, float* part_d, float* part_acc,
-                                     hipStream_t stream) {
-    switch (hq / hkv) {
-        case 1: return launch_g<1>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, chunk, max_chunks, part_m, part_d, part_acc, stream);
-        case 2: return launch_g<2>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, chunk, max_chunks, part_m, part_d, part_acc, stream);
-        case 4: return launch_g<4>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, chunk, max_chunks, part_m, part_d, part_acc, stream);
-        case 8: return launch_g<8>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, chunk, max_chunks, part_m, part_d, part_acc, stream);
-        case 16: return launch_g<16>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, chunk, max_chunks, part_m, part_d, part_acc, stream);
-        default: return hipErrorInvalidValue;
-    }
+                                     int batch, int hq, int hkv, int max_lq, const StateSlots& ss,
+                                     float sm_scale, int causal, float* part_m, float* part_d,
+                                     float* part_acc, hipStream_t stream) {
+    return dispatch(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, nullptr,
+                    nullptr, ss, part_m, part_d, part_acc, stream);
 }
 
 }  // namespace sa

@@ -180,8 +180,38 @@ sa_status_t sink_attn_prefill_split(sa_dtype_t dtype, const void *q, const void 
                                     void *stream);
 
 /*
+ * State of each query row's attention over the keys one call sees, written to one
+ * slot of a caller-chosen slot buffer, for cascade attention: the new tokens of
+ * many sequences attend a shared cached prefix in one call (all queries packed as
+ * one sequence over the prefix keys, non-causal) and their own keys in another
+ * (per sequence, causal), each call writing its own slot; sink_attn_merge_rows
+ * then combines the slots.  This is the section's split along the KV sequence
+ * with the two key sets as the blocks; the sink belongs to exactly one of them,
+ * so it enters this call's states only when include_sink is 1.
+ *
+ * Keys, masking and arguments are those of sink_attn_prefill (one block holding
+ * every visible key).  For every row r and head h the state after all of the
+ * row's visible keys, (m natural-log units, d, unnormalised acc), goes to slot
+ * `slot` of
+ *   part_m, part_d  [total_q, Hq, num_slots] float32;  part_acc [total_q, Hq, num_slots, D]
+ * and no other slot is written.  A row with no visible key and no sink gets
+ * (m = -inf, d = 0, acc = 0).
+ * Errors: those of sink_attn_prefill, plus SA_EINVAL for null partial buffers,
+ * num_slots < 1, slot outside [0, num_slots), include_sink not 0 or 1.
+ * max_seqlen_q = 0 does nothing.
+ */
+sa_status_t sink_attn_prefill_state(sa_dtype_t dtype, const void *q, const void *k, const void *v,
+                                    const float *sinks, const int32_t *cu_seqlens_q,
+                                    const int32_t *cu_seqlens_k, int32_t batch,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t max_seqlen_q, int32_t max_seqlen_k, float sm_scale,
+                                    int32_t causal, int32_t include_sink, int32_t slot,
+                                    int32_t num_slots, float *part_m, float *part_d,
+                                    float *part_acc, void *stream);
+
+/*
  * Log-sum-exp combination of every slot of per-row chunk states, as written by
- * sink_attn_prefill_split (the same combination as sink_attn_merge: with
+ * sink_attn_prefill_split or sink_attn_prefill_state (the same combination as sink_attn_merge: with
  * M = max_c m_c, out = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) d_c and
  * lse = M + ln sum_c e^(m_c - M) d_c; all m_c = -inf gives out = 0, lse = -inf).
  *

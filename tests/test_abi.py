@@ -287,3 +287,33 @@ def test_qkv_bias_rope_rejects(lib, kw, status):
 
 def test_qkv_bias_rope_empty_is_a_no_op(lib):
     assert _rope(lib, tokens=0, qkv=NULL, q=NULL) == sa.SA_OK
+
+
+def _state(lib, **kw):
+    a = dict(dtype=sa.SA_BF16, q=P, k=P, v=P, sinks=P, cu_q=P, cu_k=P, batch=2, hq=64, hkv=8,
+             d=64, max_q=4096, max_k=4096, scale=0.125, causal=1, sink=1, slot=0, nslots=2,
+             pm=P, pd=P, pa=P, stream=NULL)
+    a.update(kw)
+    return lib.sink_attn_prefill_state(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pa=NULL), sa.SA_EINVAL),
+    (dict(cu_k=NULL), sa.SA_EINVAL),
+    (dict(sink=2), sa.SA_EINVAL),
+    (dict(slot=2), sa.SA_EINVAL),
+    (dict(slot=-1), sa.SA_EINVAL),
+    (dict(nslots=0), sa.SA_EINVAL),
+    (dict(causal=5), sa.SA_EINVAL),
+    (dict(hq=64, hkv=6), sa.SA_EINVAL),
+    (dict(d=128), sa.SA_EUNSUPPORTED),
+    (dict(scale=float("nan")), sa.SA_EINVAL),
+    (dict(dtype=9), sa.SA_EINVAL),
+])
+def test_prefill_state_rejects(lib, kw, status):
+    assert _state(lib, **kw) == status
+    assert lib.sink_attn_last_error().decode()
+
+
+def test_prefill_state_empty_is_a_no_op(lib):
+    assert _state(lib, max_q=0) == sa.SA_OK

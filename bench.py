@@ -120,6 +120,18 @@ def bench_decode(steps: int, warmup: int):
         graphs[i % KV_COPIES].replay()
     _sync()
     graph_ms = (time.perf_counter() - t0) * 1e3 / steps
+    # one step at a time, the host waiting for each (a serving loop that needs the
+    # result before the next step): eager launches against the captured graph
+    sync_ms = {}
+    for name, fn in (("eager", step), ("graph", lambda i: graphs[i % KV_COPIES].replay())):
+        for i in range(10):
+            fn(i)
+            torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(i)
+            torch.cuda.synchronize()
+        sync_ms[name] = (time.perf_counter() - t0) * 1e3 / steps
     # distribution of single steps (an event pair around each step adds its own gap)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for i in range(steps):
@@ -133,7 +145,7 @@ def bench_decode(steps: int, warmup: int):
     return dict(
         workload=wl.name, kv_bytes=kv_bytes, ms_per_step=ms_per_step,
         gbs=kv_bytes / (ms_per_step * 1e-3) / 1e9,
-        split_ms_mean=float(split_ms), graph_ms_per_step=graph_ms,
+        split_ms_mean=float(split_ms), graph_ms_per_step=graph_ms, sync_ms=sync_ms,
         step_ms_p10_p50_p90=[float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
         batch=wl.batch, kv_len=int(max_lk), chunk=chunk, num_chunks=nch, wl=wl)
 
@@ -525,7 +537,8 @@ def main(argv=None):
         "context_hbm_torch": context_hbm(),
         "graph_replay": {"ms_per_step": round(dec["graph_ms_per_step"], 5),
                          "value": round(dec["kv_bytes"] / (dec["graph_ms_per_step"] * 1e-3) / 1e9, 2),
-                         "unit": "GB/s"},
+                         "unit": "GB/s",
+                         "host_synced_ms_per_step": {k: round(v, 5) for k, v in dec["sync_ms"].items()}},
         "roofline": {"kernel": "decode_split_mfma<8>", "bound": "hbm",
                      "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),

@@ -9,6 +9,7 @@
 #include <cstdlib>
 #include <initializer_list>
 #include <string>
+#include <vector>
 
 #include "kernels.h"
 #include "moe_router.h"
@@ -72,6 +73,39 @@ sa_status_t check_heads(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim
     return SA_OK;
 }
 
+// With SINK_ATTN_DEBUG=1, the preconditions that live in device memory are checked
+// too, at the cost of a synchronisation: sequence offsets nondecreasing, lengths
+// within the max_seqlen_* bounds, L_q <= L_k under causal masking, sinks neither
+// +inf nor NaN.  cu_q == nullptr means one query per sequence (decode).
+sa_status_t debug_check_inputs(hipStream_t stream, const int32_t* cu_q, const int32_t* cu_k,
+                               int32_t batch, int32_t max_q, int32_t max_k, int32_t causal,
+                               const float* sinks, int32_t hq) {
+    if (!debug_sync()) return SA_OK;
+    hipError_t e = hipStreamSynchronize(stream);
+    std::vector<int32_t> hq_cu(batch + 1, 0), hk_cu(batch + 1, 0);
+    std::vector<float> hs(sinks ? hq : 0);
+    if (e == hipSuccess && cu_q)
+        e = hipMemcpy(hq_cu.data(), cu_q, sizeof(int32_t) * (batch + 1), hipMemcpyDeviceToHost);
+    if (e == hipSuccess && cu_k)
+        e = hipMemcpy(hk_cu.data(), cu_k, sizeof(int32_t) * (batch + 1), hipMemcpyDeviceToHost);
+    if (e == hipSuccess && sinks)
+        e = hipMemcpy(hs.data(), sinks, sizeof(float) * hq, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(SA_ELAUNCH, "debug input check: %s", hipGetErrorString(e));
+    for (int32_t b = 0; b < batch; ++b) {
+        const int64_t lk = (int64_t)hk_cu[b + 1] - hk_cu[b];
+        const int64_t lq = cu_q ? (int64_t)hq_cu[b + 1] - hq_cu[b] : 1;
+        if (lk < 0 || lq < 0)
+            return fail(SA_EINVAL, "debug: cu_seqlens decrease at sequence %d", b);
+        if (lk > max_k) return fail(SA_EINVAL, "debug: sequence %d has %lld keys > max_seqlen_k %d", b, (long long)lk, max_k);
+        if (cu_q && lq > max_q) return fail(SA_EINVAL, "debug: sequence %d has %lld queries > max_seqlen_q %d", b, (long long)lq, max_q);
+        if (cu_q && causal && lq > lk) return fail(SA_EINVAL, "debug: sequence %d has L_q %lld > L_k %lld under causal masking", b, (long long)lq, (long long)lk);
+    }
+    for (int32_t h = 0; h < (int32_t)hs.size(); ++h)
+        if (std::isnan(hs[h]) || hs[h] == INFINITY)
+            return fail(SA_EINVAL, "debug: sink of head %d is %f (must be finite or -inf)", h, hs[h]);
+    return SA_OK;
+}
+
 // A launch's x dimension counts work-items in 32 bits: blocks * threads per block
 // must stay below 2^32.
 sa_status_t check_grid(int64_t blocks, int64_t threads_per_block, const char* what) {
@@ -117,6 +151,7 @@ sa_status_t sink_attn_prefill(sa_dtype_t dtype, const void* q, const void* k, co
     if (max_seqlen_q == 0) return ok();
     if ((s = check_device()) != SA_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((s = debug_check_inputs(st, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k, causal, sinks, num_q_heads)) != SA_OK) return s;
     hipError_t e;
     if (mfma)
         e = sa::launch_mfma_prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, batch, num_q_heads,
@@ -166,6 +201,7 @@ sa_status_t sink_attn_prefill_split(sa_dtype_t dtype, const void* q, const void*
     if (max_seqlen_q == 0) return ok();
     if ((s = check_device()) != SA_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((s = debug_check_inputs(st, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k, causal, sinks, num_q_heads)) != SA_OK) return s;
     hipError_t e;
     const sa::StateSlots ss{kv_chunk_size, max_num_chunks, max_num_chunks, 0, 1};
     if (mfma)
@@ -215,6 +251,7 @@ sa_status_t sink_attn_prefill_state(sa_dtype_t dtype, const void* q, const void*
     if (max_seqlen_q == 0) return ok();
     if ((s = check_device()) != SA_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((s = debug_check_inputs(st, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k, causal, sinks, num_q_heads)) != SA_OK) return s;
     // one chunk starting at key 0 that no sequence outgrows
     const sa::StateSlots ss{0x7fffffff, 1, num_slots, slot, include_sink};
     hipError_t e;
@@ -309,6 +346,7 @@ sa_status_t sink_attn_decode_split(sa_dtype_t dtype, const void* q, const void* 
     if (s != SA_OK) return s;
     if ((s = check_device()) != SA_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((s = debug_check_inputs(st, nullptr, cu_seqlens_k, batch, 1, max_seqlen_k, 0, sinks, num_q_heads)) != SA_OK) return s;
     hipError_t e = launch_split(dtype, q, k, v, sinks, cu_seqlens_k, batch, num_q_heads,
                                 num_kv_heads, kv_chunk_size, max_num_chunks, sm_scale, part_m,
                                 part_d, part_acc, st);
@@ -328,6 +366,7 @@ sa_status_t sink_attn_decode(sa_dtype_t dtype, const void* q, const void* k, con
     if (!out) return fail(SA_EINVAL, "sink_attn_decode: null pointer argument");
     if ((s = check_device()) != SA_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((s = debug_check_inputs(st, nullptr, cu_seqlens_k, batch, 1, max_seqlen_k, 0, sinks, num_q_heads)) != SA_OK) return s;
     hipError_t e = launch_split(dtype, q, k, v, sinks, cu_seqlens_k, batch, num_q_heads,
                                 num_kv_heads, kv_chunk_size, max_num_chunks, sm_scale, part_m,
                                 part_d, part_acc, st);

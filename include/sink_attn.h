@@ -42,7 +42,15 @@
  *     synchronisation and are the caller's duty: monotone cu_seqlens,
  *     L_q <= L_k for every sequence under causal masking, per-sequence
  *     lengths no larger than the max_seqlen_* bounds given, sinks that are
- *     finite or -inf (never +inf or NaN).
+ *     finite or -inf (never +inf or NaN).  Broken ones give wrong results, not
+ *     out-of-bounds accesses: no kernel reads or writes outside the rows and
+ *     slots the host-side arguments describe.
+ *   - Debugging aid: with SINK_ATTN_DEBUG=1 in the environment (read once per
+ *     process), the attention entry points synchronise `stream`, copy the
+ *     sequence offsets and sinks to the host and check the preconditions
+ *     above (SA_EINVAL), and synchronise again after the launch so that a
+ *     failing kernel is reported as SA_ELAUNCH.  This is slow and must not be
+ *     used while the stream is being captured into a graph.
  */
 #ifndef SINK_ATTN_H
 #define SINK_ATTN_H

@@ -35,9 +35,14 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     """float32 -> bf16 bit patterns (uint16), round to nearest, ties to even."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     u = x.view(np.uint32)
-    # modulo-2^32 sums: the top 16 bits are those of the exact sum (which is < 2^33)
-    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
-    return rounded.astype(np.uint16)
+    # modulo-2^32 sums: the top 16 bits are those of the exact sum (which is < 2^33);
+    # in place, one temporary
+    r = u >> np.uint32(16)
+    r &= np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
+    return r.astype(np.uint16)
 
 
 def bf16_widen(bits: np.ndarray) -> np.ndarray:

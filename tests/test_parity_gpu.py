@@ -471,3 +471,27 @@ def test_long_kv_split_prefill_bench_shape(orc):
     ref, ref_lse = orc.workload(wl, rows=rows, nthreads=NTHREADS)
     H.assert_close(out[rows], ref, bf16=True)
     H.assert_lse_close(lse[rows], ref_lse, bf16=True)
+
+
+# ---------------------------------------------------------------- many short sequences
+
+def test_many_short_sequences_prefill(orc):
+    """2000 causal sequences of 1..40 tokens over 0..60 cached keys each (16/2 heads):
+    the packed varlen indexing at a large batch, every row checked."""
+    wl = W.random_case(101, batch=2000, hq=16, hkv=2, max_q=40, max_k=100)
+    dev = H.Device(wl)
+    out, lse = H.run_prefill(dev)
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    H.assert_close(out, ref, bf16=True)
+    H.assert_lse_close(lse, ref_lse, bf16=True)
+
+
+def test_many_short_sequences_decode(orc):
+    """4096 single-token sequences of 1..300 keys (16/2 heads), 64-key chunks, through
+    the one-call decode; every sequence checked."""
+    wl = W.random_case(102, batch=4096, hq=16, hkv=2, max_k=300, decode=True)
+    dev = H.Device(wl)
+    out, lse = H.run_decode_call(dev, 64)
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    H.assert_close(out, ref, bf16=True)
+    H.assert_lse_close(lse, ref_lse, bf16=True)

@@ -240,6 +240,37 @@ def library_gemm_tflops(n: int = 8192, steps: int = 50, warmup: int = 20) -> flo
     return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
 
 
+def bench_prefill_groups(groups=(1, 2, 4, 16), steps: int = 50):
+    """The causal prefill shape (4 x 4096, 64 query heads) with other group sizes
+    (Hkv = 64 / G): TFLOP/s per G, as context for the G = 8 line."""
+    import torch
+    import gqa_attention_head_amd as sa
+    from gqa_attention_head_amd import workloads as W
+
+    dev = torch.device("cuda", 0)
+    res = {}
+    for g in groups:
+        wl = W.make_workload(f"prefill_bf16_b4_s4096_h64g{g}_d64", dtype="bf16", kind="prefill",
+                             seqlens_q=[4096] * 4, seqlens_k=[4096] * 4, num_q_heads=64,
+                             num_kv_heads=64 // g, head_dim=64, seed=3, causal=True)
+        up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        q, k, v = up(wl.q16), up(wl.k16), up(wl.v16)
+        sinks = torch.from_numpy(wl.sinks).to(dev)
+        cu = torch.from_numpy(wl.cu_q).to(dev)
+        out = torch.empty_like(q)
+        step = lambda i: sa.prefill(q, k, v, sinks, cu, cu, 4096, 4096, wl.sm_scale, causal=True, out=out)
+        warm_up(step, 20, 30.0)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for i in range(steps):
+            step(i)
+        ev[1].record()
+        _sync()
+        ms = ev[0].elapsed_time(ev[1]) / steps
+        res[f"G{g}"] = {"ms": round(ms, 4), "tflops": round(wl.prefill_flops() / (ms * 1e-3) / 1e12, 1)}
+    return res
+
+
 LONG_KV = dict(lq=256, lk=131072, chunk=16384)  # chunked prefill over a long cache
 
 
@@ -506,6 +537,7 @@ def main(argv=None):
     dec = bench_decode(args.steps, args.warmup)
     pre = None if args.no_prefill else bench_prefill(args.prefill_steps, 50)
     long_kv = None if args.no_prefill else bench_prefill_long_kv(max(10, args.prefill_steps // 2), 20)
+    groups = None if args.no_prefill else bench_prefill_groups()
     router = None if args.no_prefill else bench_router(200, 50)
     epilogue = None if args.no_prefill else bench_epilogue(200, 50)
     cpu = None
@@ -561,6 +593,8 @@ def main(argv=None):
                 "prefill_over_gemm": round(pre["tflops"] / pre["gemm_tflops"], 4)}}
     if long_kv is not None:
         line["prefill_long_kv"] = long_kv
+    if groups is not None:
+        line["prefill"]["other_group_sizes"] = groups
     if router is not None:
         router["roofline"]["traffic"] = traffic.get("router")
         line["router"] = router

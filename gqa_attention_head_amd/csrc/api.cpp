@@ -106,6 +106,10 @@ sa_status_t debug_check_inputs(hipStream_t stream, const int32_t* cu_q, const in
     return SA_OK;
 }
 
+// Query blocks the MFMA prefill launches cover, rounded up to the multiple of eight
+// that bounds its workgroup grouping (G < 8 puts 8 / G blocks in one workgroup).
+int64_t qblocks_bound(int32_t max_seqlen_q) { return ((int64_t)(max_seqlen_q + 31) / 32 + 7) / 8 * 8; }
+
 // A launch's x dimension counts work-items in 32 bits: blocks * threads per block
 // must stay below 2^32.
 sa_status_t check_grid(int64_t blocks, int64_t threads_per_block, const char* what) {
@@ -144,7 +148,7 @@ sa_status_t sink_attn_prefill(sa_dtype_t dtype, const void* q, const void* k, co
         return fail(SA_EINVAL, "sm_scale must be finite and > 0");
     const int group = num_q_heads / num_kv_heads;
     const bool mfma = dtype == SA_BF16 && sa::mfma_prefill_supported(group);
-    if (mfma && (s = check_grid((int64_t)batch * num_kv_heads * ((max_seqlen_q + 31) / 32),
+    if (mfma && (s = check_grid((int64_t)batch * num_kv_heads * qblocks_bound(max_seqlen_q),
                                 64 * group, "sink_attn_prefill")) != SA_OK)
         return s;
     if (!mfma && (s = check_grid(max_seqlen_q, 64, "sink_attn_prefill")) != SA_OK) return s;
@@ -190,7 +194,7 @@ sa_status_t sink_attn_prefill_split(sa_dtype_t dtype, const void* q, const void*
     const int group = num_q_heads / num_kv_heads;
     const bool mfma = dtype == SA_BF16 && sa::mfma_prefill_supported(group);
     if (mfma) {
-        if ((s = check_grid((int64_t)batch * num_kv_heads * ((max_seqlen_q + 31) / 32) * max_num_chunks,
+        if ((s = check_grid((int64_t)batch * num_kv_heads * qblocks_bound(max_seqlen_q) * max_num_chunks,
                             64 * group, "sink_attn_prefill_split")) != SA_OK)
             return s;
     } else if ((int64_t)batch * max_num_chunks > 65535) {
@@ -242,7 +246,7 @@ sa_status_t sink_attn_prefill_state(sa_dtype_t dtype, const void* q, const void*
     const int group = num_q_heads / num_kv_heads;
     const bool mfma = dtype == SA_BF16 && sa::mfma_prefill_supported(group);
     if (mfma) {
-        if ((s = check_grid((int64_t)batch * num_kv_heads * ((max_seqlen_q + 31) / 32), 64 * group,
+        if ((s = check_grid((int64_t)batch * num_kv_heads * qblocks_bound(max_seqlen_q), 64 * group,
                             "sink_attn_prefill_state")) != SA_OK)
             return s;
     } else if ((s = check_grid(max_seqlen_q, 64, "sink_attn_prefill_state")) != SA_OK) {

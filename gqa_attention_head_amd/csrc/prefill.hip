@@ -75,56 +75,66 @@ __device__ __forceinline__ float exp_tile(const f32x16 (&s)[2], float scale_log2
 // only, and only when ss.sink is set; a chunk a row cannot see leaves
 // (m = -inf, d = 0, acc = 0).
 template <int G, bool kSplit>
-__global__ __launch_bounds__(64 * G) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(64 * (G >= 8 ? G : 8)) __attribute__((amdgpu_waves_per_eu(4)))
 void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                   const uint16_t* __restrict__ v, const float* __restrict__ sinks,
                   const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int hq,
-                  int hkv, int batch, int n_qblocks, float scale_log2, int causal,
+                  int hkv, int batch, int n_qgroups, float scale_log2, int causal,
                   uint16_t* __restrict__ out, float* __restrict__ lse, StateSlots ss,
                   float* __restrict__ part_m, float* __restrict__ part_d,
                   float* __restrict__ part_acc) {
-    constexpr int kThreads = 64 * G;
+    // A workgroup has kQB * G waves: the G query heads of KV head g for kQB
+    // consecutive 32-row query blocks (kQB = 8 / G below eight heads), so it always
+    // has at least eight waves sharing each K/V tile.
+    constexpr int kQB = G >= 8 ? 1 : 8 / G;
+    constexpr int kThreads = 64 * G * kQB;
     constexpr int kPer = (kSegs + kThreads - 1) / kThreads;
     __shared__ uint16_t kl[2][kBK * kStride];
     __shared__ uint16_t vl[2][kBK * kVStride];
 
-    // Work item -> (sequence b, KV head g, query block qb).  Query blocks go
-    // heaviest first (the causal triangle gives late blocks the most keys).
+    // Work item -> (sequence b, KV head g, group of kQB query blocks qg).  Query
+    // blocks go heaviest first (the causal triangle gives late blocks the most keys).
     // When the (b, g) pairs split evenly over the 8 XCDs (workgroups are dealt
     // to XCDs round-robin), each XCD keeps its own pairs, so a K/V head is
     // cached in one XCD's L2 only.
     const int pairs = batch * hkv;
-    const int per_chunk = pairs * n_qblocks;
+    const int per_chunk = pairs * n_qgroups;
     const int c = kSplit ? (int)(blockIdx.x / per_chunk) : 0;
     const int bid = kSplit ? (int)(blockIdx.x % per_chunk) : (int)blockIdx.x;
-    int pair, qb;
+    int pair, qg;
     if (pairs % 8 == 0) {
         const int xcd = bid % 8, j = bid / 8, per_xcd = pairs / 8;
         pair = (j % per_xcd) * 8 + xcd;
-        qb = n_qblocks - 1 - j / per_xcd;
+        qg = n_qgroups - 1 - j / per_xcd;
     } else {
         pair = bid % pairs;
-        qb = n_qblocks - 1 - bid / pairs;
+        qg = n_qgroups - 1 - bid / pairs;
     }
     const int b = pair / hkv, g = pair % hkv;
     const int q0 = cu_q[b], lq = cu_q[b + 1] - q0;
     const int k0 = cu_k[b], lk = cu_k[b + 1] - k0;
-    const int r0 = qb * kBQ;
-    if (r0 >= lq) return;  // uniform over the workgroup
+    const int r0g = qg * kQB * kBQ;  // first row of the workgroup's query blocks
+    if (r0g >= lq) return;           // uniform over the workgroup
 
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    const int h = g * G + wave;
+    const int h = g * G + wave % G;
+    const int r0 = r0g + (wave / G) * kBQ;  // this wave's query block
     const int l32 = lane % 32, half = lane / 32;
     const int row = r0 + l32;
     const bool row_ok = row < lq;
+    const bool wave_live = r0 < lq;  // a wave past the last row only helps stage K/V
     const int last = min(r0 + kBQ, lq) - 1;
-    // keys [0, kend) are visible to some row of the block; [0, full_end) to every row.
+    const int last_wg = min(r0g + kQB * kBQ, lq) - 1;
+    // keys [0, kend) are visible to some row of the wave's block, [0, kend_wg) to some
+    // row of the workgroup, [0, full_end) to every row of the wave's block.
     int kend = causal ? max(0, min(lk, lk - lq + last + 1)) : lk;
+    int kend_wg = causal ? max(0, min(lk, lk - lq + last_wg + 1)) : lk;
     int full_end = causal ? max(0, min(lk, lk - lq + r0 + 1)) : lk;
     // this launch's keys start at k_lo (0 unless split); rows see keys below row_lim
     const int k_lo = kSplit ? c * ss.chunk : 0;
     if (kSplit) {
         kend = min(kend, k_lo + ss.chunk);
+        kend_wg = min(kend_wg, k_lo + ss.chunk);
         full_end = min(full_end, k_lo + ss.chunk);
     }
     const int row_lim = min(kend, causal ? lk - lq + row + 1 : lk);
@@ -175,9 +185,9 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
         }
     };
 
-    // 64-key tiles t_first .. ntiles - 1 cover [k_lo, kend)
+    // 64-key tiles t_first .. ntiles - 1 cover [k_lo, kend_wg)
     const int t_first = k_lo / kBK;
-    const int ntiles = (kend > k_lo) ? ceil_div(kend, kBK) : t_first;
+    const int ntiles = (kend_wg > k_lo) ? ceil_div(kend_wg, kBK) : t_first;
     if (ntiles > t_first) {
         gload(t_first * kBK);
         lstore(t_first & 1);
@@ -211,44 +221,48 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
             if (key >= row_lim || key < k_lo) s[kb][i] = kNegInf;                                \
         }                                                                                        \
     }
-        f32x16 s[2];
-        SA_SCORES()
-        bf16x8 pb[4];
-        float psum;
-        // no finite reference yet (no sink and no visible key so far): take the max
-        bool need_max = __any(m == kNegInf);
-        if (!need_max) {
-            psum = exp_tile(s, scale_log2, m, pb);
-            need_max = __any(!(psum <= kSumLimit));
-        }
-        if (need_max) {  // rare: recompute the scores rather than keep them live
+        // a wave whose block sees none of this tile's keys only helps stage K/V
+        // (uniform per wave; always true with one query block per workgroup)
+        if (kQB == 1 || (wave_live && j0 < kend)) {
+            f32x16 s[2];
             SA_SCORES()
-            float tmax = kNegInf;
+            bf16x8 pb[4];
+            float psum;
+            // no finite reference yet (no sink and no visible key so far): take the max
+            bool need_max = __any(m == kNegInf);
+            if (!need_max) {
+                psum = exp_tile(s, scale_log2, m, pb);
+                need_max = __any(!(psum <= kSumLimit));
+            }
+            if (need_max) {  // rare: recompute the scores rather than keep them live
+                SA_SCORES()
+                float tmax = kNegInf;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kb][i]);
-            const float m_new = fmaxf(m, max_xor32(tmax) * scale_log2);
-            const float alpha = (m == kNegInf) ? 0.0f : fast_exp2(m - m_new);
-            dl *= alpha;
+                    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[kb][i]);
+                const float m_new = fmaxf(m, max_xor32(tmax) * scale_log2);
+                const float alpha = (m == kNegInf) ? 0.0f : fast_exp2(m - m_new);
+                dl *= alpha;
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) o[mt] *= alpha;
-            m = m_new;
-            const float msub = (m == kNegInf) ? 0.0f : m;
-            psum = exp_tile(s, scale_log2, msub, pb);
-        }
+                for (int mt = 0; mt < 2; ++mt) o[mt] *= alpha;
+                m = m_new;
+                const float msub = (m == kNegInf) ? 0.0f : m;
+                psum = exp_tile(s, scale_log2, msub, pb);
+            }
 #undef SA_SCORES
-        dl += psum;
+            dl += psum;
 
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int key_base = 32 * (ks / 2) + 16 * (ks % 2);
+            for (int ks = 0; ks < 4; ++ks) {
+                const int key_base = 32 * (ks / 2) + 16 * (ks % 2);
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const uint16_t* p0 = vt + (key_base + 4 * half + c16 / 4) * kVStride + 32 * mt +
-                                     16 * (g4 % 2) + 4 * (c16 % 4);
-                const bf16x8 va = concat(lds_read_tr16(p0), lds_read_tr16(p0 + 8 * kVStride));
-                o[mt] = mfma32x32x16(va, pb[ks], o[mt]);
+                for (int mt = 0; mt < 2; ++mt) {
+                    const uint16_t* p0 = vt + (key_base + 4 * half + c16 / 4) * kVStride + 32 * mt +
+                                         16 * (g4 % 2) + 4 * (c16 % 4);
+                    const bf16x8 va = concat(lds_read_tr16(p0), lds_read_tr16(p0 + 8 * kVStride));
+                    o[mt] = mfma32x32x16(va, pb[ks], o[mt]);
+                }
             }
         }
         if (more) lstore(buf ^ 1);
@@ -299,18 +313,20 @@ hipError_t launch_g(const void* q, const void* k, const void* v, const float* si
                     int max_lq, float sm_scale, int causal, void* out, float* lse,
                     const StateSlots& ss, float* part_m, float* part_d, float* part_acc,
                     hipStream_t stream) {
-    const int n_qblocks = ceil_div(max_lq, kBQ);
+    constexpr int kQB = G >= 8 ? 1 : 8 / G;  // query blocks per workgroup
+    const int n_qgroups = ceil_div(ceil_div(max_lq, kBQ), kQB);
     const bool split = part_m != nullptr;
-    const int64_t blocks = (int64_t)batch * hkv * n_qblocks * (split ? ss.n_chunks : 1);
+    const int64_t blocks = (int64_t)batch * hkv * n_qgroups * (split ? ss.n_chunks : 1);
+    const dim3 threads(64 * G * kQB);
     if (split)
-        hipLaunchKernelGGL((prefill_mfma<G, true>), dim3((unsigned)blocks), dim3(64 * G), 0,
+        hipLaunchKernelGGL((prefill_mfma<G, true>), dim3((unsigned)blocks), threads, 0,
                            stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                           sinks, cu_q, cu_k, hq, hkv, batch, n_qblocks, sm_scale * kLog2e, causal,
+                           sinks, cu_q, cu_k, hq, hkv, batch, n_qgroups, sm_scale * kLog2e, causal,
                            nullptr, nullptr, ss, part_m, part_d, part_acc);
     else
-        hipLaunchKernelGGL((prefill_mfma<G, false>), dim3((unsigned)blocks), dim3(64 * G), 0,
+        hipLaunchKernelGGL((prefill_mfma<G, false>), dim3((unsigned)blocks), threads, 0,
                            stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                           sinks, cu_q, cu_k, hq, hkv, batch, n_qblocks, sm_scale * kLog2e, causal,
+                           sinks, cu_q, cu_k, hq, hkv, batch, n_qgroups, sm_scale * kLog2e, causal,
                            (uint16_t*)out, lse, ss, nullptr, nullptr, nullptr);
     return hipGetLastError();
 }

@@ -495,3 +495,39 @@ def test_many_short_sequences_decode(orc):
     ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
     H.assert_close(out, ref, bf16=True)
     H.assert_lse_close(lse, ref_lse, bf16=True)
+
+
+# ---------------------------------------------------------------- seeded random configurations
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_configurations(orc, seed):
+    """Seeded random shapes: group size, KV heads, batch, lengths, causal or not, dtype and
+    chunk lengths drawn per seed; prefill, split prefill + row merge and one-call decode
+    each against the oracle."""
+    rng = np.random.default_rng(1000 + seed)
+    group = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    hkv = int(rng.integers(1, 4))
+    dtype = "bf16" if rng.random() < 0.75 else "fp32"
+    causal = bool(rng.random() < 0.7)
+    batch = int(rng.integers(1, 6))
+    max_q = int(rng.integers(1, 150))
+    max_k = max_q + int(rng.integers(0, 300))
+    wl = W.random_case(2000 + seed, dtype=dtype, batch=batch, hq=hkv * group, hkv=hkv,
+                       max_q=max_q, max_k=max_k, causal=causal,
+                       sink_sigma=float(rng.choice([1.0, 4.0])))
+    bf16 = dtype == "bf16"
+    dev = H.Device(wl)
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    out, lse = H.run_prefill(dev)
+    H.assert_close(out, ref, bf16=bf16)
+    H.assert_lse_close(lse, ref_lse, bf16=bf16)
+    chunk = int(rng.integers(1, max(2, dev.max_lk + 1)))
+    _, _, _, sout, slse = run_prefill_split(dev, chunk)
+    H.assert_close(sout, ref, bf16=bf16)
+    H.assert_lse_close(slse, ref_lse, bf16=bf16)
+    # decode: each sequence's last query row, which sees all of its keys either way
+    last = (wl.cu_q[1:] - 1).astype(np.int64)
+    qd = dev.q[torch.from_numpy(last).cuda()].contiguous()
+    dout, dlse = H.run_decode_call(dev, int(rng.integers(1, 200)), q=qd)
+    H.assert_close(dout, ref[last], bf16=bf16)
+    H.assert_lse_close(dlse, ref_lse[last], bf16=bf16)

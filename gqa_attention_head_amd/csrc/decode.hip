@@ -229,9 +229,7 @@ hipError_t launch_g(const void* q, const void* k, const void* v, const float* si
 
 }  // namespace
 
-bool mfma_decode_supported(int group) {
-    return group == 1 || group == 2 || group == 4 || group == 8 || group == 16;
-}
+bool mfma_decode_supported(int group) { return group >= 1 && group <= 16; }
 
 hipError_t launch_mfma_decode_split(const void* q, const void* k, const void* v,
                                     const float* sinks, const int32_t* cu_k, int batch, int hq,
@@ -239,11 +237,10 @@ hipError_t launch_mfma_decode_split(const void* q, const void* k, const void* v,
                                     float* part_m, float* part_d, float* part_acc,
                                     hipStream_t stream) {
     switch (hq / hkv) {
-        case 1: return launch_g<1>(q, k, v, sinks, cu_k, batch, hq, hkv, chunk, max_chunks, sm_scale, part_m, part_d, part_acc, stream);
-        case 2: return launch_g<2>(q, k, v, sinks, cu_k, batch, hq, hkv, chunk, max_chunks, sm_scale, part_m, part_d, part_acc, stream);
-        case 4: return launch_g<4>(q, k, v, sinks, cu_k, batch, hq, hkv, chunk, max_chunks, sm_scale, part_m, part_d, part_acc, stream);
-        case 8: return launch_g<8>(q, k, v, sinks, cu_k, batch, hq, hkv, chunk, max_chunks, sm_scale, part_m, part_d, part_acc, stream);
-        case 16: return launch_g<16>(q, k, v, sinks, cu_k, batch, hq, hkv, chunk, max_chunks, sm_scale, part_m, part_d, part_acc, stream);
+#define SA_CASE(GG) case GG: return launch_g<GG>(q, k, v, sinks, cu_k, batch, hq, hkv, chunk, max_chunks, sm_scale, part_m, part_d, part_acc, stream);
+        SA_CASE(1) SA_CASE(2) SA_CASE(3) SA_CASE(4) SA_CASE(5) SA_CASE(6) SA_CASE(7) SA_CASE(8)
+        SA_CASE(9) SA_CASE(10) SA_CASE(11) SA_CASE(12) SA_CASE(13) SA_CASE(14) SA_CASE(15) SA_CASE(16)
+#undef SA_CASE
         default: return hipErrorInvalidValue;
     }
 }

@@ -75,7 +75,7 @@ __device__ __forceinline__ float exp_tile(const f32x16 (&s)[2], float scale_log2
 // only, and only when ss.sink is set; a chunk a row cannot see leaves
 // (m = -inf, d = 0, acc = 0).
 template <int G, bool kSplit>
-__global__ __launch_bounds__(64 * (G >= 8 ? G : 8)) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(64 * G * (G >= 8 ? 1 : 8 / G)) __attribute__((amdgpu_waves_per_eu(4)))
 void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                   const uint16_t* __restrict__ v, const float* __restrict__ sinks,
                   const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int hq,
@@ -84,8 +84,9 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
                   float* __restrict__ part_m, float* __restrict__ part_d,
                   float* __restrict__ part_acc) {
     // A workgroup has kQB * G waves: the G query heads of KV head g for kQB
-    // consecutive 32-row query blocks (kQB = 8 / G below eight heads), so it always
-    // has at least eight waves sharing each K/V tile.
+    // consecutive 32-row query blocks (kQB = 8 / G, rounded down, below eight heads),
+    // so it has (up to) eight waves sharing each K/V tile and two or more workgroups
+    // fit a compute unit.
     constexpr int kQB = G >= 8 ? 1 : 8 / G;
     constexpr int kThreads = 64 * G * kQB;
     constexpr int kPer = (kSegs + kThreads - 1) / kThreads;
@@ -338,7 +339,8 @@ hipError_t dispatch(const void* q, const void* k, const void* v, const float* si
                     hipStream_t stream) {
     switch (hq / hkv) {
 #define SA_CASE(GG) case GG: return launch_g<GG>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, ss, part_m, part_d, part_acc, stream);
-        SA_CASE(1) SA_CASE(2) SA_CASE(4) SA_CASE(8) SA_CASE(16)
+        SA_CASE(1) SA_CASE(2) SA_CASE(3) SA_CASE(4) SA_CASE(5) SA_CASE(6) SA_CASE(7) SA_CASE(8)
+        SA_CASE(9) SA_CASE(10) SA_CASE(11) SA_CASE(12) SA_CASE(13) SA_CASE(14) SA_CASE(15) SA_CASE(16)
 #undef SA_CASE
         default: return hipErrorInvalidValue;
     }
@@ -346,9 +348,7 @@ hipError_t dispatch(const void* q, const void* k, const void* v, const float* si
 
 }  // namespace
 
-bool mfma_prefill_supported(int group) {
-    return group == 1 || group == 2 || group == 4 || group == 8 || group == 16;
-}
+bool mfma_prefill_supported(int group) { return group >= 1 && group <= 16; }
 
 hipError_t launch_mfma_prefill(const void* q, const void* k, const void* v, const float* sinks,
                                const int32_t* cu_q, const int32_t* cu_k, int batch, int hq,

@@ -316,7 +316,8 @@ sa_status_t check_split_args(sa_dtype_t dtype, const void* q, const void* k, con
                     max_num_chunks, (long long)need);
     if (!(std::isfinite(sm_scale) && sm_scale > 0.0f))
         return fail(SA_EINVAL, "sm_scale must be finite and > 0");
-    if ((s = check_grid((int64_t)batch * max_num_chunks * ((num_kv_heads + 7) / 8), 512, "decode")) != SA_OK)
+    // one wave per (KV head, slice of at most 16 query heads), eight per workgroup
+    if ((s = check_grid((int64_t)batch * max_num_chunks * ((num_q_heads + 7) / 8), 512, "decode")) != SA_OK)
         return s;
     return SA_OK;
 }

@@ -13,7 +13,10 @@
 // K/V are token-major ([token][kv head][64]), so the 8 waves together stream
 // whole contiguous 1 KB token rows: workgroups never read a fraction of a
 // DRAM row that another workgroup reads later.  Each wave keeps kDepth tiles
-// of loads in flight in registers, read with nontemporal loads.
+// of loads in flight in registers, read with nontemporal loads.  Above 16 query
+// heads per KV head, the heads are cut into slices of G, one wave each; the waves
+// of one KV head then read the same K/V rows, with cached loads so that the later
+// ones hit in the cache.
 //
 //
 // Per 32-key tile and wave:
@@ -42,6 +45,12 @@ struct DecodeTile {
     u32x4 vr[4];       // four 16-byte V segments (rows lane/8 + 8r)
 };
 
+template <bool kStream>
+__device__ __forceinline__ u32x4 load_kv(const uint16_t* p) {
+    return kStream ? load_stream(p) : *reinterpret_cast<const u32x4*>(p);
+}
+
+template <bool kStream>
 __device__ __forceinline__ void load_tile(DecodeTile& t, const uint16_t* __restrict__ kbase,
                                           const uint16_t* __restrict__ vbase, int row_stride,
                                           int t0, int hi, int lane) {
@@ -50,13 +59,13 @@ __device__ __forceinline__ void load_tile(DecodeTile& t, const uint16_t* __restr
     for (int kb = 0; kb < 2; ++kb) {
         const int key = min(t0 + 16 * kb + c16, hi - 1);
         const uint16_t* kp = kbase + (int64_t)key * row_stride + 8 * q4;
-        t.ka[kb][0] = __builtin_bit_cast(bf16x8, load_stream(kp));
-        t.ka[kb][1] = __builtin_bit_cast(bf16x8, load_stream(kp + 32));
+        t.ka[kb][0] = __builtin_bit_cast(bf16x8, load_kv<kStream>(kp));
+        t.ka[kb][1] = __builtin_bit_cast(bf16x8, load_kv<kStream>(kp + 32));
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int key = min(t0 + lane / 8 + 8 * r, hi - 1);
-        t.vr[r] = load_stream(vbase + (int64_t)key * row_stride + 8 * (lane % 8));
+        t.vr[r] = load_kv<kStream>(vbase + (int64_t)key * row_stride + 8 * (lane % 8));
     }
     // Keep the loads where they are issued: the scheduler would otherwise move
     // them next to their first use and the prefetch would be lost.
@@ -120,7 +129,7 @@ __device__ __forceinline__ void process_tile(WaveState& st, const DecodeTile& cu
     }
 }
 
-template <int G, int kDepth, int kHeadsPerBlock>
+template <int G, int kDepth, int kHeadsPerBlock, bool kHeadSlices = false>
 __global__ __launch_bounds__(64 * kHeadsPerBlock) void decode_split_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ sinks,
@@ -144,11 +153,17 @@ __global__ __launch_bounds__(64 * kHeadsPerBlock) void decode_split_mfma(
     const int hi = min(lo + chunk, len);
 
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    const int g = hb * kHeadsPerBlock + wave;
+    // kHeadSlices: more than 16 query heads share a KV head; wave unit u covers
+    // slice u % slices (G heads) of KV head u / slices.
+    const int group = kHeadSlices ? hq / hkv : G;
+    const int slices = group / G;
+    const int u = hb * kHeadsPerBlock + wave;
+    const int g = kHeadSlices ? u / slices : u;
+    const int hs = kHeadSlices ? u % slices : 0;
     const bool g_ok = g < hkv;
     const int q4 = lane / 16, c16 = lane % 16;
     const bool head_ok = g_ok && c16 < G;
-    const int h = g * G + c16;
+    const int h = g * group + hs * G + c16;
     const int row_stride = hkv * kD;
     const int gsafe = g_ok ? g : 0;
     const uint16_t* kbase = k + ((int64_t)k0 * hkv + gsafe) * kD;
@@ -182,14 +197,14 @@ __global__ __launch_bounds__(64 * kHeadsPerBlock) void decode_split_mfma(
         DecodeTile buf[kDepth];
 #pragma unroll
         for (int d = 0; d < kDepth; ++d)
-            load_tile(buf[d], kbase, vbase, row_stride, lo + d * kTile, hi, lane);
+            load_tile<!kHeadSlices>(buf[d], kbase, vbase, row_stride, lo + d * kTile, hi, lane);
         int it = 0;
         do {
 #pragma unroll
             for (int d = 0; d < kDepth; ++d) {
                 const int ts = lo + (it + d) * kTile;
                 process_tile(st, buf[d], qb0, qb1, vw, ts, hi, scale_log2, lane);
-                load_tile(buf[d], kbase, vbase, row_stride, ts + kDepth * kTile, hi, lane);
+                load_tile<!kHeadSlices>(buf[d], kbase, vbase, row_stride, ts + kDepth * kTile, hi, lane);
             }
             it += kDepth;
         } while (it < ntiles);
@@ -212,37 +227,52 @@ __global__ __launch_bounds__(64 * kHeadsPerBlock) void decode_split_mfma(
     }
 }
 
-template <int G>
+template <int G, bool kHeadSlices>
 hipError_t launch_g(const void* q, const void* k, const void* v, const float* sinks,
                     const int32_t* cu_k, int batch, int hq, int hkv, int chunk, int max_chunks,
                     float sm_scale, float* part_m, float* part_d, float* part_acc,
                     hipStream_t stream) {
     constexpr int kDepth = 2, kHeadsPerBlock = 8;
-    const int head_blocks = ceil_div(hkv, kHeadsPerBlock);
+    const int units = hkv * ((hq / hkv) / G);  // (KV head, slice of G query heads)
+    const int head_blocks = ceil_div(units, kHeadsPerBlock);
     const int64_t blocks = (int64_t)batch * max_chunks * head_blocks;
-    hipLaunchKernelGGL((decode_split_mfma<G, kDepth, kHeadsPerBlock>), dim3((unsigned)blocks),
-                       dim3(64 * kHeadsPerBlock), 0, stream, (const uint16_t*)q, (const uint16_t*)k,
-                       (const uint16_t*)v, sinks, cu_k, hq, hkv, chunk, max_chunks, head_blocks,
-                       sm_scale * kLog2e, part_m, part_d, part_acc);
+    hipLaunchKernelGGL((decode_split_mfma<G, kDepth, kHeadsPerBlock, kHeadSlices>),
+                       dim3((unsigned)blocks), dim3(64 * kHeadsPerBlock), 0, stream,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, sinks, cu_k, hq,
+                       hkv, chunk, max_chunks, head_blocks, sm_scale * kLog2e, part_m, part_d,
+                       part_acc);
     return hipGetLastError();
 }
 
 }  // namespace
 
-bool mfma_decode_supported(int group) { return group >= 1 && group <= 16; }
+bool mfma_decode_supported(int group) { return group >= 1 && group <= 64; }
 
 hipError_t launch_mfma_decode_split(const void* q, const void* k, const void* v,
                                     const float* sinks, const int32_t* cu_k, int batch, int hq,
                                     int hkv, int chunk, int max_chunks, float sm_scale,
                                     float* part_m, float* part_d, float* part_acc,
                                     hipStream_t stream) {
-    switch (hq / hkv) {
-#define SA_CASE(GG) case GG: return launch_g<GG>(q, k, v, sinks, cu_k, batch, hq, hkv, chunk, max_chunks, sm_scale, part_m, part_d, part_acc, stream);
+    const int group = hq / hkv;
+#define SA_ARGS q, k, v, sinks, cu_k, batch, hq, hkv, chunk, max_chunks, sm_scale, part_m, part_d, part_acc, stream
+    switch (group) {
+#define SA_CASE(GG) case GG: return launch_g<GG, false>(SA_ARGS);
         SA_CASE(1) SA_CASE(2) SA_CASE(3) SA_CASE(4) SA_CASE(5) SA_CASE(6) SA_CASE(7) SA_CASE(8)
         SA_CASE(9) SA_CASE(10) SA_CASE(11) SA_CASE(12) SA_CASE(13) SA_CASE(14) SA_CASE(15) SA_CASE(16)
 #undef SA_CASE
-        default: return hipErrorInvalidValue;
+        default: break;
     }
+    // more than 16 heads per KV head: slices of the largest divisor of the group
+    // that is at most 16 and a power of two (one wave per slice)
+    if (group > 16 && group <= 64) {
+        if (group % 16 == 0) return launch_g<16, true>(SA_ARGS);
+        if (group % 8 == 0) return launch_g<8, true>(SA_ARGS);
+        if (group % 4 == 0) return launch_g<4, true>(SA_ARGS);
+        if (group % 2 == 0) return launch_g<2, true>(SA_ARGS);
+        return launch_g<1, true>(SA_ARGS);
+    }
+#undef SA_ARGS
+    return hipErrorInvalidValue;
 }
 
 }  // namespace sa

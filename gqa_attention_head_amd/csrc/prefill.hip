@@ -7,11 +7,13 @@
 // family serves prefill and decode.  The whole KV range of a query block is
 // one block here, so the sink enters the state once, at the start.
 //
-// Work decomposition.  One workgroup per (sequence b, KV head g, 32-row query
-// block); wave w of the workgroup handles query head g*G + w, so the G query
-// heads that share KV head g (grouped-query attention) share every K/V tile
-// the workgroup stages in LDS.  Query blocks are issued heaviest first (the
-// causal triangle gives late blocks the most keys).
+// Work decomposition.  One workgroup per (sequence b, KV head g, group of 32-row
+// query blocks); each wave handles one query head that shares KV head g
+// (grouped-query attention) for one query block, so all of them share every K/V
+// tile the workgroup stages in LDS.  Below eight heads per KV head a workgroup
+// takes several consecutive query blocks; above sixteen the heads are cut into
+// slices, one workgroup each.  Query blocks are issued heaviest first (the causal
+// triangle gives late blocks the most keys).
 //
 // Per 64-key tile and wave (scores kept transposed, S^T = K Q^T, so that the
 // exponentiated tile is already laid out as the B operand of the PV product):
@@ -74,7 +76,7 @@ __device__ __forceinline__ float exp_tile(const f32x16 (&s)[2], float scale_log2
 // (row, head), instead of the normalised output.  The sink enters chunk 0's state
 // only, and only when ss.sink is set; a chunk a row cannot see leaves
 // (m = -inf, d = 0, acc = 0).
-template <int G, bool kSplit>
+template <int G, bool kSplit, bool kHeadSlices = false>
 __global__ __launch_bounds__(64 * G * (G >= 8 ? 1 : 8 / G)) __attribute__((amdgpu_waves_per_eu(4)))
 void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                   const uint16_t* __restrict__ v, const float* __restrict__ sinks,
@@ -98,10 +100,16 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     // When the (b, g) pairs split evenly over the 8 XCDs (workgroups are dealt
     // to XCDs round-robin), each XCD keeps its own pairs, so a K/V head is
     // cached in one XCD's L2 only.
+    // kHeadSlices: more than G query heads share KV head g; the group's
+    // group / G slices of G heads each go to separate workgroups (slice hs slowest).
     const int pairs = batch * hkv;
-    const int per_chunk = pairs * n_qgroups;
+    const int group = kHeadSlices ? hq / hkv : G;
+    const int per_slice = pairs * n_qgroups;
+    const int per_chunk = per_slice * (group / G);
     const int c = kSplit ? (int)(blockIdx.x / per_chunk) : 0;
-    const int bid = kSplit ? (int)(blockIdx.x % per_chunk) : (int)blockIdx.x;
+    const int rest = kSplit ? (int)(blockIdx.x % per_chunk) : (int)blockIdx.x;
+    const int hs = kHeadSlices ? rest / per_slice : 0;
+    const int bid = kHeadSlices ? rest % per_slice : rest;
     int pair, qg;
     if (pairs % 8 == 0) {
         const int xcd = bid % 8, j = bid / 8, per_xcd = pairs / 8;
@@ -118,7 +126,7 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     if (r0g >= lq) return;           // uniform over the workgroup
 
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    const int h = g * G + wave % G;
+    const int h = g * group + hs * G + wave % G;
     const int r0 = r0g + (wave / G) * kBQ;  // this wave's query block
     const int l32 = lane % 32, half = lane / 32;
     const int row = r0 + l32;
@@ -308,7 +316,7 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
         lse[orow] = empty ? kNegInf : (m + fast_log2(dsum)) * kLn2;
 }
 
-template <int G>
+template <int G, bool kHeadSlices>
 hipError_t launch_g(const void* q, const void* k, const void* v, const float* sinks,
                     const int32_t* cu_q, const int32_t* cu_k, int batch, int hq, int hkv,
                     int max_lq, float sm_scale, int causal, void* out, float* lse,
@@ -316,16 +324,18 @@ hipError_t launch_g(const void* q, const void* k, const void* v, const float* si
                     hipStream_t stream) {
     constexpr int kQB = G >= 8 ? 1 : 8 / G;  // query blocks per workgroup
     const int n_qgroups = ceil_div(ceil_div(max_lq, kBQ), kQB);
+    const int slices = (hq / hkv) / G;      // workgroups per (sequence, KV head, block group)
     const bool split = part_m != nullptr;
-    const int64_t blocks = (int64_t)batch * hkv * n_qgroups * (split ? ss.n_chunks : 1);
+    const int64_t blocks =
+        (int64_t)batch * hkv * n_qgroups * slices * (split ? ss.n_chunks : 1);
     const dim3 threads(64 * G * kQB);
     if (split)
-        hipLaunchKernelGGL((prefill_mfma<G, true>), dim3((unsigned)blocks), threads, 0,
+        hipLaunchKernelGGL((prefill_mfma<G, true, kHeadSlices>), dim3((unsigned)blocks), threads, 0,
                            stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                            sinks, cu_q, cu_k, hq, hkv, batch, n_qgroups, sm_scale * kLog2e, causal,
                            nullptr, nullptr, ss, part_m, part_d, part_acc);
     else
-        hipLaunchKernelGGL((prefill_mfma<G, false>), dim3((unsigned)blocks), threads, 0,
+        hipLaunchKernelGGL((prefill_mfma<G, false, kHeadSlices>), dim3((unsigned)blocks), threads, 0,
                            stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                            sinks, cu_q, cu_k, hq, hkv, batch, n_qgroups, sm_scale * kLog2e, causal,
                            (uint16_t*)out, lse, ss, nullptr, nullptr, nullptr);
@@ -337,18 +347,31 @@ hipError_t dispatch(const void* q, const void* k, const void* v, const float* si
                     int max_lq, float sm_scale, int causal, void* out, float* lse,
                     const StateSlots& ss, float* part_m, float* part_d, float* part_acc,
                     hipStream_t stream) {
-    switch (hq / hkv) {
-#define SA_CASE(GG) case GG: return launch_g<GG>(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, ss, part_m, part_d, part_acc, stream);
+    const int group = hq / hkv;
+#define SA_ARGS q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, ss, part_m, part_d, part_acc, stream
+    switch (group) {
+#define SA_CASE(GG) case GG: return launch_g<GG, false>(SA_ARGS);
         SA_CASE(1) SA_CASE(2) SA_CASE(3) SA_CASE(4) SA_CASE(5) SA_CASE(6) SA_CASE(7) SA_CASE(8)
         SA_CASE(9) SA_CASE(10) SA_CASE(11) SA_CASE(12) SA_CASE(13) SA_CASE(14) SA_CASE(15) SA_CASE(16)
 #undef SA_CASE
-        default: return hipErrorInvalidValue;
+        default: break;
     }
+    // more than 16 heads per KV head: slices of the largest power of two <= 16 that
+    // divides the group
+    if (group > 16 && group <= 64) {
+        if (group % 16 == 0) return launch_g<16, true>(SA_ARGS);
+        if (group % 8 == 0) return launch_g<8, true>(SA_ARGS);
+        if (group % 4 == 0) return launch_g<4, true>(SA_ARGS);
+        if (group % 2 == 0) return launch_g<2, true>(SA_ARGS);
+        return launch_g<1, true>(SA_ARGS);
+    }
+#undef SA_ARGS
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-bool mfma_prefill_supported(int group) { return group >= 1 && group <= 16; }
+bool mfma_prefill_supported(int group) { return group >= 1 && group <= 64; }
 
 hipError_t launch_mfma_prefill(const void* q, const void* k, const void* v, const float* sinks,
                                const int32_t* cu_q, const int32_t* cu_k, int batch, int hq,

@@ -101,7 +101,7 @@ def test_prefill_state_slot(orc, dtype, group, include_sink, causal):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-@pytest.mark.parametrize("group", [8, 4, 3])
+@pytest.mark.parametrize("group", [8, 4, 3, 32])
 def test_cascade_shared_prefix(orc, dtype, group):
     """Shared prefix of 1000 keys, four sequences with 1..300 new tokens each: the
     prefix call (all new tokens as one non-causal row block, sink included) and the

@@ -133,7 +133,7 @@ def test_split_invariance(orc, chunk):
     H.assert_lse_close(lse, ref_lse, bf16=True)
 
 
-@pytest.mark.parametrize("group", [1, 2, 3, 4, 5, 6, 7, 8, 12, 16])
+@pytest.mark.parametrize("group", [1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 17, 24, 32, 64])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_group_sizes_prefill(orc, group, dtype):
     wl = W.random_case(30 + group, dtype=dtype, batch=3, hq=2 * group, hkv=2, max_q=150,
@@ -145,7 +145,7 @@ def test_group_sizes_prefill(orc, group, dtype):
     H.assert_lse_close(lse, ref_lse, bf16=dtype == "bf16")
 
 
-@pytest.mark.parametrize("group", [1, 2, 3, 4, 5, 6, 7, 8, 12, 16])
+@pytest.mark.parametrize("group", [1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 17, 24, 32, 64])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_group_sizes_decode(orc, group, dtype):
     wl = W.random_case(50 + group, dtype=dtype, batch=4, hq=2 * group, hkv=2, max_k=700,
@@ -277,7 +277,7 @@ def test_decode_call_ragged_long(orc):
     H.assert_lse_close(lse, ref_lse, bf16=True)
 
 
-@pytest.mark.parametrize("group", [1, 2, 3, 4, 5, 6, 7, 8, 12, 16])
+@pytest.mark.parametrize("group", [1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 17, 24, 32, 64])
 @pytest.mark.parametrize("chunk", [37, 256, 4096])
 def test_decode_call_cases(orc, group, chunk):
     wl = W.random_case(70 + group, batch=5, hq=2 * group, hkv=2, max_k=1500, decode=True,
@@ -349,7 +349,7 @@ def run_prefill_split(dev: "H.Device", chunk: int, causal=None):
     return pm, pd, pa, out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("group", [1, 2, 3, 4, 5, 6, 7, 8, 12, 16])
+@pytest.mark.parametrize("group", [1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 17, 24, 32, 64])
 @pytest.mark.parametrize("chunk", [64, 100, 1024])
 @pytest.mark.parametrize("causal", [True, False])
 def test_prefill_split_cases(orc, group, chunk, causal):

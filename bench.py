@@ -571,7 +571,7 @@ def main(argv=None):
                          "value": round(dec["kv_bytes"] / (dec["graph_ms_per_step"] * 1e-3) / 1e9, 2),
                          "unit": "GB/s",
                          "host_synced_ms_per_step": {k: round(v, 5) for k, v in dec["sync_ms"].items()}},
-        "roofline": {"kernel": "decode_split_mfma<8>", "bound": "hbm",
+        "roofline": {"kernel": "decode_split_mfma<8, 2, 8, false>", "bound": "hbm",
                      "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic.get("decode"),
@@ -583,7 +583,7 @@ def main(argv=None):
             "workload": pre["workload"], "value": round(pre["tflops"], 2), "unit": "TFLOP/s",
             "ms": round(pre["ms_mean"], 4), "flops": pre["flops"],
             "ms_p10_p50_p90": [round(x, 4) for x in pre["ms_p10_p50_p90"]],
-            "roofline": {"kernel": "prefill_mfma<8, false>", "bound": "mfma",
+            "roofline": {"kernel": "prefill_mfma<8, false, false>", "bound": "mfma",
                          "achieved": round(pre["tflops"], 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(pre["tflops"] / BF16_PEAK_TFLOPS, 4),
                          "traffic": traffic.get("prefill"), "algorithmic_flops": pre["flops"]},

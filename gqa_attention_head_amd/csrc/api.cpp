@@ -106,9 +106,9 @@ sa_status_t debug_check_inputs(hipStream_t stream, const int32_t* cu_q, const in
     return SA_OK;
 }
 
-// Query blocks the MFMA prefill launches cover, rounded up to the multiple of eight
-// that bounds its workgroup grouping (G < 8 puts 8 / G blocks in one workgroup).
-int64_t qblocks_bound(int32_t max_seqlen_q) { return ((int64_t)(max_seqlen_q + 31) / 32 + 7) / 8 * 8; }
+// Bound on the query blocks the MFMA prefill launches cover: its workgroups group
+// up to 16 consecutive blocks, so the count is rounded up by less than 16.
+int64_t qblocks_bound(int32_t max_seqlen_q) { return (int64_t)(max_seqlen_q + 31) / 32 + 15; }
 
 // A launch's x dimension counts work-items in 32 bits: blocks * threads per block
 // must stay below 2^32.

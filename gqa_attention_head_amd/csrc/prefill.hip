@@ -76,8 +76,15 @@ __device__ __forceinline__ float exp_tile(const f32x16 (&s)[2], float scale_log2
 // (row, head), instead of the normalised output.  The sink enters chunk 0's state
 // only, and only when ss.sink is set; a chunk a row cannot see leaves
 // (m = -inf, d = 0, acc = 0).
+// Consecutive 32-row query blocks per workgroup: the G query heads of a KV head for
+// kQB blocks make G * kQB waves, which all share each K/V tile the workgroup stages.
+// Up to 8 waves where G divides 8 (two workgroups per compute unit); below eight heads
+// otherwise, up to 16 waves (G = 3, 5, 6, 7 leave 8-wave workgroups short of threads
+// to stage a tile with one 16-byte load each, and the second load spilled registers).
+constexpr int query_blocks(int G) { return G >= 8 ? 1 : (8 % G == 0 ? 8 / G : 16 / G); }
+
 template <int G, bool kSplit, bool kHeadSlices = false>
-__global__ __launch_bounds__(64 * G * (G >= 8 ? 1 : 8 / G)) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(64 * G * query_blocks(G)) __attribute__((amdgpu_waves_per_eu(4)))
 void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                   const uint16_t* __restrict__ v, const float* __restrict__ sinks,
                   const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int hq,
@@ -85,11 +92,8 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
                   uint16_t* __restrict__ out, float* __restrict__ lse, StateSlots ss,
                   float* __restrict__ part_m, float* __restrict__ part_d,
                   float* __restrict__ part_acc) {
-    // A workgroup has kQB * G waves: the G query heads of KV head g for kQB
-    // consecutive 32-row query blocks (kQB = 8 / G, rounded down, below eight heads),
-    // so it has (up to) eight waves sharing each K/V tile and two or more workgroups
-    // fit a compute unit.
-    constexpr int kQB = G >= 8 ? 1 : 8 / G;
+    // kQB * G waves: the G query heads of KV head g for kQB consecutive query blocks
+    constexpr int kQB = query_blocks(G);
     constexpr int kThreads = 64 * G * kQB;
     constexpr int kPer = (kSegs + kThreads - 1) / kThreads;
     __shared__ uint16_t kl[2][kBK * kStride];
@@ -322,7 +326,7 @@ hipError_t launch_g(const void* q, const void* k, const void* v, const float* si
                     int max_lq, float sm_scale, int causal, void* out, float* lse,
                     const StateSlots& ss, float* part_m, float* part_d, float* part_acc,
                     hipStream_t stream) {
-    constexpr int kQB = G >= 8 ? 1 : 8 / G;  // query blocks per workgroup
+    constexpr int kQB = query_blocks(G);  // query blocks per workgroup
     const int n_qgroups = ceil_div(ceil_div(max_lq, kBQ), kQB);
     const int slices = (hq / hkv) / G;      // workgroups per (sequence, KV head, block group)
     const bool split = part_m != nullptr;

@@ -197,13 +197,33 @@ def bench_prefill(steps: int, warmup: int):
                 tflops=flops / (mean_ms * 1e-3) / 1e12, wl=wl, gemm_tflops=library_gemm_tflops())
 
 
-def context_hbm():
-    """Context for the HBM roofline: what torch's own kernels sustain on this GPU, a
-    reduction (reads 2 GiB) and a copy (reads and writes 1 GiB)."""
+def read_ceiling(copies: int = 5, nbytes: int = 268435456, steps: int = 50):
+    """The device's practical streaming-read rate: the library's read yardstick
+    (nontemporal 16-byte loads, the decode's K/V access) over `copies` rotated buffers
+    of the decode's K/V size, so the last-level cache cannot serve repeats."""
     import torch
+    import gqa_attention_head_amd as sa
+    bufs = [torch.ones(nbytes // 4, device="cuda", dtype=torch.int32) for _ in range(copies)]
+    out = torch.empty(1024, device="cuda", dtype=torch.int32)
+    warm_up(lambda i: sa.read_probe(bufs[i % copies], 1024, out), 50, 60.0)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for i in range(steps):
+        sa.read_probe(bufs[i % copies], 1024, out)
+    ev[1].record()
+    _sync()
+    del bufs
+    return round(nbytes / (ev[0].elapsed_time(ev[1]) / steps * 1e-3) / 1e9, 1)
+
+
+def context_hbm():
+    """Context for the HBM roofline: the library's streaming-read yardstick, and what
+    torch's own kernels sustain on this GPU, a reduction (reads 2 GiB) and a copy (reads
+    and writes 1 GiB)."""
+    import torch
+    res = {"read_probe_gbs": read_ceiling()}
     x = torch.ones(1 << 30, device="cuda", dtype=torch.bfloat16)
     y = torch.empty(1 << 29, device="cuda", dtype=torch.bfloat16)
-    res = {}
     for name, fn, nbytes in (("sum_read_gbs", lambda: x.sum(dtype=torch.float32), 2 << 30),
                              ("copy_gbs", lambda: y.copy_(x[: 1 << 29]), 2 << 30)):
         for _ in range(5):
@@ -547,6 +567,7 @@ def main(argv=None):
 
     kernel_gbs = dec["kv_bytes"] / (dec["split_ms_mean"] * 1e-3) / 1e9
     traffic = measured_traffic()
+    hbm_ctx = context_hbm()
     line = {
         "metric": METRIC,
         "value": round(dec["gbs"], 2),
@@ -566,7 +587,7 @@ def main(argv=None):
                    "kv_copies_rotated": KV_COPIES, "parallelism": "single-gpu"},
         "hbm_frac": round(dec["gbs"] / HBM_PEAK_GBS, 4),
         "step_ms_p10_p50_p90": [round(x, 5) for x in dec["step_ms_p10_p50_p90"]],
-        "context_hbm_torch": context_hbm(),
+        "context_hbm": hbm_ctx,
         "graph_replay": {"ms_per_step": round(dec["graph_ms_per_step"], 5),
                          "value": round(dec["kv_bytes"] / (dec["graph_ms_per_step"] * 1e-3) / 1e9, 2),
                          "unit": "GB/s",
@@ -576,7 +597,8 @@ def main(argv=None):
                      "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic.get("decode"),
                      "algorithmic_bytes": dec["kv_bytes"],
-                     "launch_ms_mean": round(dec["split_ms_mean"], 5)},
+                     "launch_ms_mean": round(dec["split_ms_mean"], 5),
+                     "frac_of_read_probe": round(kernel_gbs / hbm_ctx["read_probe_gbs"], 4)},
     }
     if pre is not None:
         line["prefill"] = {

@@ -23,7 +23,7 @@ SA_FP32, SA_BF16 = 0, 1
 EXPORTS = ("sink_attn_prefill", "sink_attn_decode_split", "sink_attn_merge",
            "sink_attn_decode", "sink_attn_prefill_split", "sink_attn_merge_rows",
            "sink_attn_last_error", "moe_topk_softmax", "qkv_bias_rope",
-           "sink_attn_prefill_state")
+           "sink_attn_prefill_state", "sink_attn_read_probe")
 
 
 class SinkAttnError(RuntimeError):
@@ -75,6 +75,8 @@ def load_library():
     lib.qkv_bias_rope.restype = ctypes.c_int
     lib.qkv_bias_rope.argtypes = [vp, vp, vp, vp, ctypes.c_int64, i32, i32, i32, i32, vp, vp, vp,
                                   vp]
+    lib.sink_attn_read_probe.restype = ctypes.c_int
+    lib.sink_attn_read_probe.argtypes = [vp, ctypes.c_int64, i32, vp, vp]
     lib.sink_attn_last_error.restype = ctypes.c_char_p
     lib.sink_attn_last_error.argtypes = []
     _lib = lib
@@ -436,3 +438,23 @@ def qkv_bias_rope(qkv, bias, positions, cos_sin, num_q_heads, num_kv_heads, q=No
                              num_q_heads, num_kv_heads, d, cos_sin.shape[0], _ptr(outs[0]),
                              _ptr(outs[1]), _ptr(outs[2]), _stream(stream)))
     return tuple(outs)
+
+
+def read_probe(buf, num_blocks=1024, out=None, stream=None):
+    """Measurement utility (``sink_attn_read_probe``): one nontemporal 16-byte-load pass
+    over the bytes of the contiguous device tensor ``buf``; returns the per-workgroup XOR
+    digests (uint32 values in an int32 tensor [num_blocks]), whose XOR is the XOR of every
+    32-bit word of ``buf``."""
+    torch = _torch()
+    lib = load_library()
+    if not (buf.is_cuda and buf.is_contiguous()):
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if out is None:
+        out = torch.empty(num_blocks, device=buf.device, dtype=torch.int32)
+    _dev(out, "out", torch.int32)
+    if out.numel() < num_blocks:
+        raise ValueError("out must hold num_blocks values")
+    _check(lib.sink_attn_read_probe(_ptr(buf), nbytes, int(num_blocks), _ptr(out),
+                                    _stream(stream)))
+    return out

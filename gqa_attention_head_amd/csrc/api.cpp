@@ -14,6 +14,7 @@
 #include "kernels.h"
 #include "moe_router.h"
 #include "qkv_epilogue.h"
+#include "sa_measure.h"
 #include "sink_attn.h"
 
 namespace {
@@ -445,6 +446,23 @@ sa_status_t qkv_bias_rope(const void* qkv, const void* bias, const int32_t* posi
     hipError_t e = sa::launch_qkv_rope(qkv, bias, positions, cos_sin, num_tokens, num_q_heads,
                                        num_kv_heads, table_rows, q, k, v, st);
     return finish_launch(e, st, "qkv_bias_rope");
+}
+
+sa_status_t sink_attn_read_probe(const void* buf, int64_t bytes, int32_t num_blocks,
+                                 uint32_t* out, void* stream) {
+    if ((!buf && bytes != 0) || !out)
+        return fail(SA_EINVAL, "sink_attn_read_probe: null pointer argument");
+    if (bytes < 0 || bytes % 16 != 0)
+        return fail(SA_EINVAL, "sink_attn_read_probe: bytes must be >= 0 and a multiple of 16");
+    if (num_blocks < 1 || num_blocks > 65535)
+        return fail(SA_EINVAL, "sink_attn_read_probe: num_blocks must be in [1, 65535]");
+    if (reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+        return fail(SA_EINVAL, "sink_attn_read_probe: buf must be 16-byte aligned");
+    sa_status_t s;
+    if ((s = check_device()) != SA_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = sa::launch_read_probe(buf, bytes, num_blocks, out, st);
+    return finish_launch(e, st, "sink_attn_read_probe");
 }
 
 }  // extern "C"

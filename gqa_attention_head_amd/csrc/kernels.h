@@ -73,4 +73,10 @@ hipError_t launch_merge(bool out_bf16, const float* part_m, const float* part_d,
                         const float* part_acc, const int32_t* cu_k, int chunk, int max_chunks,
                         int batch, int hq, void* out, float* lse, hipStream_t stream);
 
+// One nontemporal 16-byte-load pass over `bytes` (a multiple of 16) of buf by
+// num_blocks workgroups of 512 threads; out[block] = XOR of the 32-bit words the
+// workgroup read.
+hipError_t launch_read_probe(const void* buf, int64_t bytes, int num_blocks, uint32_t* out,
+                             hipStream_t stream);
+
 }  // namespace sa

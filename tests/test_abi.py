@@ -317,3 +317,24 @@ def test_prefill_state_rejects(lib, kw, status):
 
 def test_prefill_state_empty_is_a_no_op(lib):
     assert _state(lib, max_q=0) == sa.SA_OK
+
+
+def _probe(lib, **kw):
+    a = dict(buf=P, nbytes=1 << 20, blocks=1024, out=P, stream=NULL)
+    a.update(kw)
+    return lib.sink_attn_read_probe(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(buf=NULL), sa.SA_EINVAL),
+    (dict(out=NULL), sa.SA_EINVAL),
+    (dict(out=NULL, nbytes=0), sa.SA_EINVAL),
+    (dict(nbytes=-16), sa.SA_EINVAL),
+    (dict(nbytes=24), sa.SA_EINVAL),            # not a multiple of 16
+    (dict(blocks=0), sa.SA_EINVAL),
+    (dict(blocks=65536), sa.SA_EINVAL),
+    (dict(buf=ctypes.c_void_p(264)), sa.SA_EINVAL),  # not 16-byte aligned
+])
+def test_read_probe_rejects(lib, kw, status):
+    assert _probe(lib, **kw) == status
+    assert lib.sink_attn_read_probe is not None and lib.sink_attn_last_error().decode()

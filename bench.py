@@ -343,6 +343,118 @@ def bench_prefill_long_kv(steps: int, warmup: int):
     return dict(workload=wl.name, flops=wl.prefill_flops(), **res)
 
 
+def _time_ms(fn, steps: int, warmup: int) -> float:
+    import torch
+    warm_up(lambda i: fn(), warmup, 60.0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    _sync()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_ragged_decode(steps: int = 30, warmup: int = 10):
+    """The long-context ragged decode (8 sequences, KV lengths of the seeded workload, 1024 to
+    131072 keys, 64/8 heads, bf16, chunk 2048): one decode call (split pass + merge) per
+    step.  K/V (1.6 GB, above the last-level cache) are drawn on the device from a seeded
+    generator: the values do not change the timing, the lengths do."""
+    import torch
+    import gqa_attention_head_amd as sa
+    from gqa_attention_head_amd import workloads as W
+
+    lens = W.ragged_decode_lengths()
+    chunk, hq, hkv, d = 2048, 64, 8, 64
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(4)
+    total = int(lens.sum())
+    k = torch.randn(total, hkv, d, device=dev, generator=g).to(torch.bfloat16)
+    v = torch.randn(total, hkv, d, device=dev, generator=g).to(torch.bfloat16)
+    q = torch.randn(len(lens), hq, d, device=dev, generator=g).to(torch.bfloat16)
+    sinks = 2.0 * torch.randn(hq, device=dev, generator=g)
+    cu_k = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
+    max_k = int(lens.max())
+    nch = -(-max_k // chunk)
+    ws = sa.DecodeWorkspace(len(lens), hq, nch, d, dev)
+    out = torch.empty_like(q)
+    ms = _time_ms(lambda: sa.decode(q, k, v, sinks, cu_k, max_k, chunk, 0.125, workspace=ws, out=out),
+                  steps, warmup)
+    kv_bytes = total * hkv * d * 2 * 2
+    del k, v
+    return {"workload": f"ragged_decode_bf16_b{len(lens)}_kv1024-131072_h64g8_d64_chunk{chunk}",
+            "kv_lengths": [int(x) for x in lens], "kv_bytes": kv_bytes, "ms": round(ms, 4),
+            "value": round(kv_bytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "hbm_frac": round(kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def bench_mixed_varlen(steps: int = 30, warmup: int = 10):
+    """The mixed packed batch (4 prefill chunks of 512-2048 new tokens over 0-8192 cached
+    keys, then 12 single-token decodes over 1024-32768 keys, 64/8 heads, bf16), two ways:
+    one prefill call over all 16 sequences, and a prefill call over the 4 chunks plus a
+    decode call (chunk 2048) over the 12 decodes, on one stream or on two.  The roofline time is
+    max(prefill flops / 2.5 PF, decode K/V bytes / 8 TB/s)."""
+    import torch
+    import gqa_attention_head_amd as sa
+    from gqa_attention_head_amd import workloads as W
+
+    wl = W.mixed_varlen()
+    dev = torch.device("cuda", 0)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, k, v = up(wl.q16), up(wl.k16), up(wl.v16)
+    sinks = torch.from_numpy(wl.sinks).to(dev)
+    cu_q = torch.from_numpy(wl.cu_q).to(dev)
+    cu_k = torch.from_numpy(wl.cu_k).to(dev)
+    lq, lk = wl.seqlens_q, wl.seqlens_k
+    npre = int((lq > 1).sum())
+    assert (lq[:npre] > 1).all() and (lq[npre:] == 1).all(), "prefill chunks come first"
+    out = torch.empty_like(q)
+    flops_pre = sum(4 * 64 * 64 * (int(a) * (int(b) - int(a)) + int(a) * (int(a) + 1) // 2)
+                    for a, b in zip(lq[:npre], lk[:npre]))
+    bytes_dec = int(lk[npre:].sum()) * 8 * 64 * 2 * 2
+    r0 = int(wl.cu_q[npre])
+    chunk = 2048
+    nch = -(-int(lk[npre:].max()) // chunk)
+    ws = sa.DecodeWorkspace(len(lq) - npre, 64, nch, 64, dev)
+    q_dec, out_dec = q[r0:], out[r0:]
+
+    def one_call():
+        sa.prefill(q, k, v, sinks, cu_q, cu_k, int(lq.max()), int(lk.max()), wl.sm_scale,
+                   causal=True, out=out)
+
+    def two_calls():
+        sa.prefill(q, k, v, sinks, cu_q[:npre + 1], cu_k[:npre + 1], int(lq[:npre].max()),
+                   int(lk[:npre].max()), wl.sm_scale, causal=True, out=out)
+        sa.decode(q_dec, k, v, sinks, cu_k[npre:], int(lk[npre:].max()), chunk, wl.sm_scale,
+                  workspace=ws, out=out_dec)
+
+    side = torch.cuda.Stream(device=dev)  # default priority
+
+    def two_streams():
+        # the MFMA-bound prefill and the HBM-bound decode overlap on two streams
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            sa.decode(q_dec, k, v, sinks, cu_k[npre:], int(lk[npre:].max()), chunk, wl.sm_scale,
+                      workspace=ws, out=out_dec)
+        sa.prefill(q, k, v, sinks, cu_q[:npre + 1], cu_k[:npre + 1], int(lq[:npre].max()),
+                   int(lk[:npre].max()), wl.sm_scale, causal=True, out=out)
+        main.wait_stream(side)
+
+    roof_ms = max(flops_pre / (BF16_PEAK_TFLOPS * 1e12), bytes_dec / (HBM_PEAK_GBS * 1e9)) * 1e3
+    res = {"workload": wl.name, "prefill_flops": flops_pre, "decode_kv_bytes": bytes_dec,
+           "roofline_ms": round(roof_ms, 4)}
+    for name, fn in (("one_prefill_call", one_call), ("prefill_plus_decode_calls", two_calls),
+                     ("prefill_and_decode_on_two_streams", two_streams)):
+        ms = _time_ms(fn, steps, warmup)
+        res[name] = {"ms": round(ms, 4), "roofline_frac": round(roof_ms / ms, 4)}
+    return res
+
+
 ROUTER = dict(tokens=1 << 20, experts=128, k=4, copies=2)
 
 
@@ -560,6 +672,8 @@ def main(argv=None):
     groups = None if args.no_prefill else bench_prefill_groups()
     router = None if args.no_prefill else bench_router(200, 50)
     epilogue = None if args.no_prefill else bench_epilogue(200, 50)
+    ragged = None if args.no_prefill else bench_ragged_decode()
+    mixed = None if args.no_prefill else bench_mixed_varlen()
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(dec["wl"], pre["wl"] if pre else __import__(
@@ -623,6 +737,10 @@ def main(argv=None):
     if epilogue is not None:
         epilogue["roofline"]["traffic"] = traffic.get("epilogue")
         line["qkv_epilogue"] = epilogue
+    if ragged is not None:
+        line["ragged_decode"] = ragged
+    if mixed is not None:
+        line["mixed_varlen"] = mixed
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)

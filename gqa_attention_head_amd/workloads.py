@@ -176,12 +176,22 @@ def causal_prefill(seed: int = 3, batch: int = 4, seqlen: int = 4096) -> Workloa
                          num_q_heads=64, num_kv_heads=8, head_dim=64, seed=seed, causal=True)
 
 
+def _ragged_lengths(rng, batch: int, lo: int, hi: int) -> np.ndarray:
+    return rng.integers(lo, hi, size=batch, endpoint=True)
+
+
+def ragged_decode_lengths(seed: int = 4, batch: int = 8, lo: int = 1024,
+                          hi: int = 131072) -> np.ndarray:
+    """The KV lengths of the long-context decode workload (its first draw from ``seed``)."""
+    return _ragged_lengths(np.random.default_rng(seed), batch, lo, hi)
+
+
 def ragged_decode(seed: int = 4, batch: int = 8, lo: int = 1024, hi: int = 131072,
                   chunk: int = 2048) -> Workload:
     """bf16 long-context decode: 8 sequences, KV length uniform in [1024, 131072], chunk 2048,
     sinks with standard deviation 2."""
     rng = np.random.default_rng(seed)
-    lens = rng.integers(lo, hi, size=batch, endpoint=True)
+    lens = _ragged_lengths(rng, batch, lo, hi)
     return make_workload(f"ragged_decode_bf16_b{batch}_kv{lo}-{hi}_h64g8_d64_chunk{chunk}",
                          dtype="bf16", kind="decode", seqlens_q=[1] * batch,
                          seqlens_k=lens.tolist(), num_q_heads=64, num_kv_heads=8,

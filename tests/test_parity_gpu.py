@@ -120,6 +120,35 @@ def test_mixed_varlen_decode_rows_via_split(orc):
     assert np.abs(pout[q_rows] - out).max() <= 2 * H.BF16_MAX_ABS
 
 
+def test_mixed_varlen_two_streams(orc):
+    """The mixed batch as a prefill call over its 4 chunks on the current stream and a
+    decode call over its 12 single-token sequences on a second stream, writing disjoint
+    rows of one output (the overlapped form bench.py times), agrees with the oracle."""
+    wl = W.mixed_varlen()
+    dev = H.Device(wl)
+    npre = 4
+    r0 = int(wl.cu_q[npre])
+    lq, lk = wl.seqlens_q, wl.seqlens_k
+    out = torch.full_like(dev.q, float("nan"))
+    ws = sa.DecodeWorkspace(len(lq) - npre, wl.num_q_heads, -(-int(lk[npre:].max()) // 2048),
+                            wl.head_dim, dev.q.device)
+    side = torch.cuda.Stream()
+    for _ in range(3):  # repeated, as timed
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            sa.decode(dev.q[r0:], dev.k, dev.v, dev.sinks, dev.cu_k[npre:], int(lk[npre:].max()),
+                      2048, wl.sm_scale, workspace=ws, out=out[r0:])
+        sa.prefill(dev.q, dev.k, dev.v, dev.sinks, dev.cu_q[:npre + 1], dev.cu_k[:npre + 1],
+                   int(lq[:npre].max()), int(lk[:npre].max()), wl.sm_scale, causal=True, out=out)
+        main.wait_stream(side)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    rows = _sample_rows(wl, per_seq=16)
+    ref, _ = orc.workload(wl, rows=rows, nthreads=NTHREADS)
+    H.assert_close(got[rows], ref, bf16=True)
+
+
 # ---------------------------------------------------------------- edge cases
 
 @pytest.mark.parametrize("chunk", [4096, 2048, 512, 64, 37, 1])

@@ -49,24 +49,39 @@ constexpr float kSumLimit = 16384.0f;  // 2^14
 
 // P^T tile in bf16, four 16-key slices (the B operand of O^T = V^T P^T): the
 // exponentials 2^(s * scale_log2 - msub) of one lane's 32 scores; returns their
-// fp32 sum (the lane's share of the running scale).
-__device__ __forceinline__ float exp_tile(const f32x16 (&s)[2], float scale_log2, float msub,
+// fp32 sum (the lane's share of the running scale).  The scores are overwritten.
+__device__ __forceinline__ float exp_tile(f32x16 (&s)[2], float scale_log2, float msub,
                                           bf16x8 (&pb)[4]) {
-    float psum = 0.0f;
+    // in place: arguments, then exponentials, then conversion and sum, so that no
+    // instruction waits on the one just issued
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = __builtin_fmaf(s[kb][i], scale_log2, -msub);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = fast_exp2(s[kb][i]);
+    __builtin_amdgcn_sched_barrier(0);
+    float pair[16];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         const int kb = ks / 2, hs = ks % 2;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * hs + 2 * e], scale_log2, -msub));
-            const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * hs + 2 * e + 1], scale_log2, -msub));
+            const float p0 = s[kb][8 * hs + 2 * e], p1 = s[kb][8 * hs + 2 * e + 1];
             const bf16x2 pk = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
             pb[ks][2 * e] = pk[0];
             pb[ks][2 * e + 1] = pk[1];
-            psum += p0 + p1;
+            pair[4 * ks + e] = p0 + p1;
         }
     }
-    return psum;
+#pragma unroll
+    for (int w = 8; w >= 1; w /= 2)
+#pragma unroll
+        for (int i = 0; i < w; ++i) pair[i] += pair[i + w];
+    return pair[0];
 }
 
 // kSplit: the keys of each sequence are cut into ss.n_chunks chunks of ss.chunk

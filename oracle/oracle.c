@@ -24,7 +24,7 @@
  * Causal masking is bottom-right aligned: with Lq queries over Lk keys, query
  * row i sits at key position Lk - Lq + i and sees keys 0 .. Lk - Lq + i.
  *
- * Three entry points:
+ * Four entry points:
  *   oracle_attention        the direct definition (max-shifted softmax over
  *                           the scores plus the sink, then the product with V)
  *   oracle_attention_split  the method as the section describes it: the keys

@@ -199,6 +199,23 @@ def test_ragged_prefill_over_cache(orc, causal):
     H.assert_lse_close(lse, ref_lse, bf16=True)
 
 
+@pytest.mark.parametrize("group", [1, 3, 8, 16, 24])
+@pytest.mark.parametrize("extra", [(0, 150, 33, 300, 700), (0, 150, 33, 300, 5000)])
+def test_prefill_over_caches_group_sizes(orc, group, extra):
+    """Causal chunks over caches of different lengths (not multiples of the 32-row
+    block) for several group sizes, with workgroups of one or several query blocks
+    and head slices; short and long caches."""
+    lq = [37, 100, 256, 1, 64]
+    wl = W.make_workload("over_caches", dtype="bf16", kind="prefill", seqlens_q=lq,
+                         seqlens_k=[a + b for a, b in zip(lq, extra)], num_q_heads=2 * group,
+                         num_kv_heads=2, head_dim=64, seed=70 + group, causal=True)
+    dev = H.Device(wl)
+    out, lse = H.run_prefill(dev)
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    H.assert_close(out, ref, bf16=True)
+    H.assert_lse_close(lse, ref_lse, bf16=True)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_empty_and_single_key_sequences(orc, dtype):
     """Decode with L = 0 (chunk 0 holds only the sink), L = 1, and a sink of -inf with no keys."""

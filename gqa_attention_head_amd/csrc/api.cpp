@@ -160,7 +160,8 @@ sa_status_t sink_attn_prefill(sa_dtype_t dtype, const void* q, const void* k, co
     hipError_t e;
     if (mfma)
         e = sa::launch_mfma_prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, batch, num_q_heads,
-                                    num_kv_heads, max_seqlen_q, sm_scale, causal, out, lse, st);
+                                    num_kv_heads, max_seqlen_q, max_seqlen_k, sm_scale, causal, out,
+                                    lse, st);
     else
         e = sa::launch_generic_prefill(dtype == SA_BF16, q, k, v, sinks, cu_seqlens_q,
                                        cu_seqlens_k, batch, num_q_heads, num_kv_heads,
@@ -211,8 +212,8 @@ sa_status_t sink_attn_prefill_split(sa_dtype_t dtype, const void* q, const void*
     const sa::StateSlots ss{kv_chunk_size, max_num_chunks, max_num_chunks, 0, 1};
     if (mfma)
         e = sa::launch_mfma_prefill_split(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, batch,
-                                          num_q_heads, num_kv_heads, max_seqlen_q, ss, sm_scale,
-                                          causal, part_m, part_d, part_acc, st);
+                                          num_q_heads, num_kv_heads, max_seqlen_q, max_seqlen_k, ss,
+                                          sm_scale, causal, part_m, part_d, part_acc, st);
     else
         e = sa::launch_generic_prefill_split(dtype == SA_BF16, q, k, v, sinks, cu_seqlens_q,
                                              cu_seqlens_k, batch, num_q_heads, num_kv_heads,
@@ -262,8 +263,8 @@ sa_status_t sink_attn_prefill_state(sa_dtype_t dtype, const void* q, const void*
     hipError_t e;
     if (mfma)
         e = sa::launch_mfma_prefill_split(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, batch,
-                                          num_q_heads, num_kv_heads, max_seqlen_q, ss, sm_scale,
-                                          causal, part_m, part_d, part_acc, st);
+                                          num_q_heads, num_kv_heads, max_seqlen_q, max_seqlen_k, ss,
+                                          sm_scale, causal, part_m, part_d, part_acc, st);
     else
         e = sa::launch_generic_prefill_split(dtype == SA_BF16, q, k, v, sinks, cu_seqlens_q,
                                              cu_seqlens_k, batch, num_q_heads, num_kv_heads,

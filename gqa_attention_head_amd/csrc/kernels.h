@@ -45,16 +45,18 @@ hipError_t launch_mfma_decode_split(const void* q, const void* k, const void* v,
                                     float* part_m, float* part_d, float* part_acc,
                                     hipStream_t stream);
 bool mfma_prefill_supported(int group);
-// Chunk states of every (query row, head, key chunk) instead of the output.
+// max_lq and max_lk bound every sequence's query and key counts (grid sizing and
+// work order).  Chunk states of every (query row, head, key chunk) instead of the output.
 hipError_t launch_mfma_prefill_split(const void* q, const void* k, const void* v,
                                      const float* sinks, const int32_t* cu_q, const int32_t* cu_k,
-                                     int batch, int hq, int hkv, int max_lq, const StateSlots& ss,
-                                     float sm_scale, int causal, float* part_m, float* part_d,
-                                     float* part_acc, hipStream_t stream);
+                                     int batch, int hq, int hkv, int max_lq, int max_lk,
+                                     const StateSlots& ss, float sm_scale, int causal,
+                                     float* part_m, float* part_d, float* part_acc,
+                                     hipStream_t stream);
 hipError_t launch_mfma_prefill(const void* q, const void* k, const void* v, const float* sinks,
                                const int32_t* cu_q, const int32_t* cu_k, int batch, int hq,
-                               int hkv, int max_lq, float sm_scale, int causal, void* out,
-                               float* lse, hipStream_t stream);
+                               int hkv, int max_lq, int max_lk, float sm_scale, int causal,
+                               void* out, float* lse, hipStream_t stream);
 
 // Top-K-then-softmax routing: bf16 logits [T, E], E in {8, ..., 512} (powers of
 // two), 1 <= k <= 8; int32 indices and bf16 weights [T, k].

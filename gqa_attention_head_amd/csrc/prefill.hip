@@ -103,7 +103,7 @@ __global__ __launch_bounds__(64 * G * query_blocks(G)) __attribute__((amdgpu_wav
 void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                   const uint16_t* __restrict__ v, const float* __restrict__ sinks,
                   const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int hq,
-                  int hkv, int batch, int n_qgroups, float scale_log2, int causal,
+                  int hkv, int batch, int n_qgroups, int pair_major, float scale_log2, int causal,
                   uint16_t* __restrict__ out, float* __restrict__ lse, StateSlots ss,
                   float* __restrict__ part_m, float* __restrict__ part_d,
                   float* __restrict__ part_acc) {
@@ -118,7 +118,10 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     // blocks go heaviest first (the causal triangle gives late blocks the most keys).
     // When the (b, g) pairs split evenly over the 8 XCDs (workgroups are dealt
     // to XCDs round-robin), each XCD keeps its own pairs, so a K/V head is
-    // cached in one XCD's L2 only.
+    // cached in one XCD's L2 only.  By default an XCD interleaves its pairs, one
+    // query group of each in turn; pair_major (rows over longer key sets, such as
+    // chunks over a cache) runs its pairs one after another instead, so that the
+    // K/V the XCD works on at a time stays within its L2.
     // kHeadSlices: more than G query heads share KV head g; the group's
     // group / G slices of G heads each go to separate workgroups (slice hs slowest).
     const int pairs = batch * hkv;
@@ -132,11 +135,11 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     int pair, qg;
     if (pairs % 8 == 0) {
         const int xcd = bid % 8, j = bid / 8, per_xcd = pairs / 8;
-        pair = (j % per_xcd) * 8 + xcd;
-        qg = n_qgroups - 1 - j / per_xcd;
+        pair = (pair_major ? j / n_qgroups : j % per_xcd) * 8 + xcd;
+        qg = n_qgroups - 1 - (pair_major ? j % n_qgroups : j / per_xcd);
     } else {
-        pair = bid % pairs;
-        qg = n_qgroups - 1 - bid / pairs;
+        pair = pair_major ? bid / n_qgroups : bid % pairs;
+        qg = n_qgroups - 1 - (pair_major ? bid % n_qgroups : bid / pairs);
     }
     const int b = pair / hkv, g = pair % hkv;
     const int q0 = cu_q[b], lq = cu_q[b + 1] - q0;
@@ -338,11 +341,12 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
 template <int G, bool kHeadSlices>
 hipError_t launch_g(const void* q, const void* k, const void* v, const float* sinks,
                     const int32_t* cu_q, const int32_t* cu_k, int batch, int hq, int hkv,
-                    int max_lq, float sm_scale, int causal, void* out, float* lse,
+                    int max_lq, int max_lk, float sm_scale, int causal, void* out, float* lse,
                     const StateSlots& ss, float* part_m, float* part_d, float* part_acc,
                     hipStream_t stream) {
     constexpr int kQB = query_blocks(G);  // query blocks per workgroup
     const int n_qgroups = ceil_div(ceil_div(max_lq, kBQ), kQB);
+    const int pair_major = max_lk > max_lq;
     const int slices = (hq / hkv) / G;      // workgroups per (sequence, KV head, block group)
     const bool split = part_m != nullptr;
     const int64_t blocks =
@@ -351,23 +355,23 @@ hipError_t launch_g(const void* q, const void* k, const void* v, const float* si
     if (split)
         hipLaunchKernelGGL((prefill_mfma<G, true, kHeadSlices>), dim3((unsigned)blocks), threads, 0,
                            stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                           sinks, cu_q, cu_k, hq, hkv, batch, n_qgroups, sm_scale * kLog2e, causal,
+                           sinks, cu_q, cu_k, hq, hkv, batch, n_qgroups, pair_major, sm_scale * kLog2e, causal,
                            nullptr, nullptr, ss, part_m, part_d, part_acc);
     else
         hipLaunchKernelGGL((prefill_mfma<G, false, kHeadSlices>), dim3((unsigned)blocks), threads, 0,
                            stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                           sinks, cu_q, cu_k, hq, hkv, batch, n_qgroups, sm_scale * kLog2e, causal,
+                           sinks, cu_q, cu_k, hq, hkv, batch, n_qgroups, pair_major, sm_scale * kLog2e, causal,
                            (uint16_t*)out, lse, ss, nullptr, nullptr, nullptr);
     return hipGetLastError();
 }
 
 hipError_t dispatch(const void* q, const void* k, const void* v, const float* sinks,
                     const int32_t* cu_q, const int32_t* cu_k, int batch, int hq, int hkv,
-                    int max_lq, float sm_scale, int causal, void* out, float* lse,
+                    int max_lq, int max_lk, float sm_scale, int causal, void* out, float* lse,
                     const StateSlots& ss, float* part_m, float* part_d, float* part_acc,
                     hipStream_t stream) {
     const int group = hq / hkv;
-#define SA_ARGS q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out, lse, ss, part_m, part_d, part_acc, stream
+#define SA_ARGS q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, max_lk, sm_scale, causal, out, lse, ss, part_m, part_d, part_acc, stream
     switch (group) {
 #define SA_CASE(GG) case GG: return launch_g<GG, false>(SA_ARGS);
         SA_CASE(1) SA_CASE(2) SA_CASE(3) SA_CASE(4) SA_CASE(5) SA_CASE(6) SA_CASE(7) SA_CASE(8)
@@ -394,20 +398,21 @@ bool mfma_prefill_supported(int group) { return group >= 1 && group <= 64; }
 
 hipError_t launch_mfma_prefill(const void* q, const void* k, const void* v, const float* sinks,
                                const int32_t* cu_q, const int32_t* cu_k, int batch, int hq,
-                               int hkv, int max_lq, float sm_scale, int causal, void* out,
-                               float* lse, hipStream_t stream) {
+                               int hkv, int max_lq, int max_lk, float sm_scale, int causal,
+                               void* out, float* lse, hipStream_t stream) {
     const StateSlots whole{0, 1, 1, 0, 1};  // one block of keys, sink included
-    return dispatch(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, out,
-                    lse, whole, nullptr, nullptr, nullptr, stream);
+    return dispatch(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, max_lk, sm_scale, causal,
+                    out, lse, whole, nullptr, nullptr, nullptr, stream);
 }
 
 hipError_t launch_mfma_prefill_split(const void* q, const void* k, const void* v,
                                      const float* sinks, const int32_t* cu_q, const int32_t* cu_k,
-                                     int batch, int hq, int hkv, int max_lq, const StateSlots& ss,
-                                     float sm_scale, int causal, float* part_m, float* part_d,
-                                     float* part_acc, hipStream_t stream) {
-    return dispatch(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, sm_scale, causal, nullptr,
-                    nullptr, ss, part_m, part_d, part_acc, stream);
+                                     int batch, int hq, int hkv, int max_lq, int max_lk,
+                                     const StateSlots& ss, float sm_scale, int causal,
+                                     float* part_m, float* part_d, float* part_acc,
+                                     hipStream_t stream) {
+    return dispatch(q, k, v, sinks, cu_q, cu_k, batch, hq, hkv, max_lq, max_lk, sm_scale, causal,
+                    nullptr, nullptr, ss, part_m, part_d, part_acc, stream);
 }
 
 }  // namespace sa

@@ -505,6 +505,28 @@ def test_long_single_sequence_prefill_sampled(orc):
     assert np.all(np.isfinite(out))
 
 
+def test_max_batch_decode_and_prefill(orc):
+    """The largest batch the entry points accept (65535 sequences), ragged 1-3 keys each,
+    G = 8 on one KV head: the decode split + merge (chunk 2, so up to 2 chunks) and the
+    prefill of the same single-token rows, checked on sampled sequences."""
+    batch = 65535
+    rng = np.random.default_rng(81)
+    lk = rng.integers(1, 3, size=batch, endpoint=True).tolist()
+    wl = W.make_workload("max_batch", dtype="bf16", kind="decode", seqlens_q=[1] * batch,
+                         seqlens_k=lk, num_q_heads=8, num_kv_heads=1, head_dim=64, seed=82,
+                         causal=False, sink_values=[-np.inf, -2.0, 0.0, 1.0, 2.0, 4.0, 0.5, -1.0])
+    dev = H.Device(wl)
+    rows = np.array([0, 1, 2, 1000, 32767, 65533, 65534], dtype=np.int64)
+    ref, ref_lse = orc.workload(wl, rows=rows, nthreads=NTHREADS)
+    out, lse = H.run_decode(dev, 2)
+    H.assert_close(out[rows], ref, bf16=True)
+    H.assert_lse_close(lse[rows], ref_lse, bf16=True)
+    assert np.all(np.isfinite(out))
+    pout, plse = H.run_prefill(dev, causal=False)
+    H.assert_close(pout[rows], ref, bf16=True)
+    H.assert_lse_close(plse[rows], ref_lse, bf16=True)
+
+
 def test_long_kv_split_prefill_bench_shape(orc):
     """The benchmark's chunked prefill: 256 new tokens over 131072 keys (64/8 heads),
     16384-key chunks, split pass then row merge; sampled rows against the oracle."""

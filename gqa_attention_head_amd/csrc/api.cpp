@@ -415,6 +415,8 @@ sa_status_t moe_topk_softmax(const void* logits, int64_t num_tokens, int32_t num
         return fail(SA_EINVAL, "k must be in [1, min(8, num_experts)], got %d", k);
     if (num_tokens == 0) return ok();  // nothing to read or write: pointers may be null
     if (!logits || !indices || !weights) return fail(SA_EINVAL, "moe_topk_softmax: null pointer argument");
+    if (reinterpret_cast<uintptr_t>(logits) % 16 != 0)
+        return fail(SA_EINVAL, "moe_topk_softmax: logits must be 16-byte aligned");
     sa_status_t s;
     if ((s = check_device()) != SA_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);

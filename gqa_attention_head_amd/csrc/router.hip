@@ -7,8 +7,10 @@
 // float32 and rounded to bf16.
 //
 // Layout: a token's E logits are spread over E/32 lanes (one lane for E < 32),
-// each reading its 32 (or E) logits as 16-byte loads, so a wave's loads cover a
-// contiguous run of whole token rows.  Each logit becomes one 32-bit key whose
+// each holding 32 (or E) logits, so a wave covers a contiguous run of whole token
+// rows.  The wave reads that run with nontemporal 16-byte loads, each instruction
+// one contiguous 1 KB, into its own LDS slice, and every lane then reads its
+// logits from there.  Each logit becomes one 32-bit key whose
 // unsigned order is the ranking: the high half maps the bf16 value to an
 // order-preserving code (-0 folded onto +0; two codes per word with packed 16-bit
 // arithmetic), the low half holds 31 - (position in the lane), so a larger key is
@@ -91,18 +93,30 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const uint16_t* __res
     const int sub = lane % kLanes, grp = lane / kLanes;
     const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / 64;
     const int64_t waves = (int64_t)gridDim.x * blockDim.x / 64;
+    // the wave's token rows, 64 * kGroups 16-byte pieces, staged through its LDS slice
+    __shared__ u32x4 stage[4][64 * kGroups];
+    u32x4* mine_lds = stage[threadIdx.x / 64];
+    const int64_t total16 = num_tokens * (E / 8);  // 16-byte pieces of the whole input
     // uniform over the wave: every lane takes part in the cross-lane maxima
     for (int64_t t0 = wave * kTokensPerWave; t0 < num_tokens; t0 += waves * kTokensPerWave) {
         const int64_t t = t0 + grp;
         const bool ok = t < num_tokens;
-        u32x4 raw[kGroups];
+        // nontemporal loads, each instruction one contiguous 1 KB of the wave's rows
+        const int64_t p0 = t0 * (E / 8);
+        u32x4 ld[kGroups];
 #pragma unroll
         for (int q = 0; q < kGroups; ++q) {
-            raw[q] = u32x4{0u, 0u, 0u, 0u};
-            // plain (cached) loads: the 4 loads of a lane hit each 128-byte line of its
-            // token row in turn, so the line must stay in the cache between them
-            if (ok) raw[q] = *reinterpret_cast<const u32x4*>(logits + t * E + kPer * sub + 8 * q);
+            const int64_t pi = p0 + q * 64 + lane;
+            ld[q] = pi < total16 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(logits) + pi)
+                                 : u32x4{0u, 0u, 0u, 0u};
         }
+        wave_lds_sync();  // the previous step's reads of the slice are done
+#pragma unroll
+        for (int q = 0; q < kGroups; ++q) mine_lds[q * 64 + lane] = ld[q];
+        wave_lds_sync();
+        u32x4 raw[kGroups];
+#pragma unroll
+        for (int q = 0; q < kGroups; ++q) raw[q] = mine_lds[grp * (E / 8) + (kPer / 8) * sub + q];
         uint32_t top[KP];
 #pragma unroll
         for (int i = 0; i < KP; ++i) top[i] = 0u;  // below every key

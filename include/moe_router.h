@@ -21,15 +21,15 @@ extern "C" {
 #endif
 
 /*
- * logits   [num_tokens, num_experts] bf16, device pointer, finite values (NaN and
- *          infinities are outside the contract)
+ * logits   [num_tokens, num_experts] bf16, device pointer, 16-byte aligned, finite
+ *          values (NaN and infinities are outside the contract)
  * indices  [num_tokens, k] int32, device pointer (written): experts in rank order
  * weights  [num_tokens, k] bf16, device pointer (written): softmax of the k
  *          selected logits, in the same order
  * num_experts in {8, 16, 32, 64, 128, 256, 512}; 1 <= k <= min(8, num_experts).
  * The caller owns every buffer; the call is asynchronous on `stream`.
  * Errors: SA_EINVAL for num_tokens < 0, k out of range or (with num_tokens > 0)
- * null pointers; SA_EUNSUPPORTED for another num_experts; SA_ELAUNCH for launch
+ * null pointers or misaligned logits; SA_EUNSUPPORTED for another num_experts; SA_ELAUNCH for launch
  * failures.  num_tokens = 0 does nothing and accepts null pointers.
  */
 sa_status_t moe_topk_softmax(const void *logits, int64_t num_tokens, int32_t num_experts,

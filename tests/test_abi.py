@@ -250,6 +250,7 @@ def _router(lib, **kw):
     (dict(experts=4, k=2), sa.SA_EUNSUPPORTED),
     (dict(experts=96), sa.SA_EUNSUPPORTED),
     (dict(experts=1024), sa.SA_EUNSUPPORTED),
+    (dict(logits=ctypes.c_void_p(258)), sa.SA_EINVAL),  # not 16-byte aligned
 ])
 def test_router_rejects(lib, kw, status):
     if status is None:

@@ -121,7 +121,8 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     // cached in one XCD's L2 only.  By default an XCD interleaves its pairs, one
     // query group of each in turn; pair_major (rows over longer key sets, such as
     // chunks over a cache) runs its pairs one after another instead, so that the
-    // K/V the XCD works on at a time stays within its L2.
+    // XCD streams the K/V of fewer heads at a time (measured faster there, slower
+    // on equal query and key counts).
     // kHeadSlices: more than G query heads share KV head g; the group's
     // group / G slices of G heads each go to separate workgroups (slice hs slowest).
     const int pairs = batch * hkv;

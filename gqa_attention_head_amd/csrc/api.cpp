@@ -2,6 +2,8 @@
 // Every check that needs only host data happens before anything is launched.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -120,6 +122,15 @@ sa_status_t check_grid(int64_t blocks, int64_t threads_per_block, const char* wh
     return SA_OK;
 }
 
+// Chunk c covers keys [c * C, (c + 1) * C); the kernels form these bounds in 32 bits
+// for every c < max_num_chunks, so max_num_chunks * C must stay below 2^31.
+sa_status_t check_chunk_span(int32_t kv_chunk_size, int32_t max_num_chunks, const char* what) {
+    if ((int64_t)kv_chunk_size * max_num_chunks > (int64_t)INT32_MAX)
+        return fail(SA_EINVAL, "%s: max_num_chunks (%d) * kv_chunk_size (%d) exceeds 2^31 - 1",
+                    what, max_num_chunks, kv_chunk_size);
+    return SA_OK;
+}
+
 sa_status_t check_dtype(sa_dtype_t d) {
     if (d != SA_FP32 && d != SA_BF16) return fail(SA_EINVAL, "unknown dtype %d", (int)d);
     return SA_OK;
@@ -191,6 +202,8 @@ sa_status_t sink_attn_prefill_split(sa_dtype_t dtype, const void* q, const void*
     if (max_num_chunks < need)
         return fail(SA_EINVAL, "max_num_chunks (%d) < ceil(max_seqlen_k / kv_chunk_size) = %lld",
                     max_num_chunks, (long long)need);
+    if ((s = check_chunk_span(kv_chunk_size, max_num_chunks, "sink_attn_prefill_split")) != SA_OK)
+        return s;
     if (!(std::isfinite(sm_scale) && sm_scale > 0.0f))
         return fail(SA_EINVAL, "sm_scale must be finite and > 0");
     const int group = num_q_heads / num_kv_heads;
@@ -299,41 +312,97 @@ sa_status_t sink_attn_merge_rows(sa_dtype_t out_dtype, const float* part_m, cons
 
 namespace {
 
+// kv_chunk_size == 0 (balanced ranges) is valid only where allow_balanced is set.
 sa_status_t check_split_args(sa_dtype_t dtype, const void* q, const void* k, const void* v,
                              const float* sinks, const int32_t* cu_seqlens_k, int32_t batch,
                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                              int32_t max_seqlen_k, int32_t kv_chunk_size, int32_t max_num_chunks,
                              float sm_scale, const float* part_m, const float* part_d,
-                             const float* part_acc) {
+                             const float* part_acc, bool allow_balanced) {
     sa_status_t s;
     if ((s = check_dtype(dtype)) != SA_OK) return s;
     if (!q || !k || !v || !sinks || !cu_seqlens_k || !part_m || !part_d || !part_acc)
         return fail(SA_EINVAL, "decode: null pointer argument");
     if ((s = check_heads(batch, num_q_heads, num_kv_heads, head_dim)) != SA_OK) return s;
-    if (kv_chunk_size < 1) return fail(SA_EINVAL, "kv_chunk_size must be >= 1, got %d", kv_chunk_size);
+    if (kv_chunk_size < 0 || (kv_chunk_size == 0 && !allow_balanced))
+        return fail(SA_EINVAL, "kv_chunk_size must be >= %d, got %d", allow_balanced ? 0 : 1, kv_chunk_size);
     if (max_seqlen_k < 0) return fail(SA_EINVAL, "max_seqlen_k must be >= 0");
-    const int64_t need = max_seqlen_k == 0 ? 1 : ((int64_t)max_seqlen_k + kv_chunk_size - 1) / kv_chunk_size;
-    if (max_num_chunks < need)
-        return fail(SA_EINVAL, "max_num_chunks (%d) < ceil(max_seqlen_k / kv_chunk_size) = %lld",
-                    max_num_chunks, (long long)need);
+    if (kv_chunk_size > 0) {
+        const int64_t need = max_seqlen_k == 0 ? 1 : ((int64_t)max_seqlen_k + kv_chunk_size - 1) / kv_chunk_size;
+        if (max_num_chunks < need)
+            return fail(SA_EINVAL, "max_num_chunks (%d) < ceil(max_seqlen_k / kv_chunk_size) = %lld",
+                        max_num_chunks, (long long)need);
+        if ((s = check_chunk_span(kv_chunk_size, max_num_chunks, "decode")) != SA_OK) return s;
+    } else if (max_num_chunks < 1) {
+        return fail(SA_EINVAL, "max_num_chunks must be >= 1, got %d", max_num_chunks);
+    }
     if (!(std::isfinite(sm_scale) && sm_scale > 0.0f))
         return fail(SA_EINVAL, "sm_scale must be finite and > 0");
-    // one wave per (KV head, slice of at most 16 query heads), eight per workgroup
-    if ((s = check_grid((int64_t)batch * max_num_chunks * ((num_q_heads + 7) / 8), 512, "decode")) != SA_OK)
+    // fixed chunks: one workgroup per (sequence, chunk slot, block of eight waves, one
+    // wave per KV head or slice of at most 16 query heads)
+    if (kv_chunk_size > 0 &&
+        (s = check_grid((int64_t)batch * max_num_chunks * ((num_q_heads + 7) / 8), 512, "decode")) != SA_OK)
         return s;
+    return SA_OK;
+}
+
+// Compute units of the current device (the balanced decode gives each one range).
+int compute_units() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64 && cached[dev].load(std::memory_order_relaxed) > 0)
+        return cached[dev].load(std::memory_order_relaxed);
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+        n = 256;
+    if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// The key blocks of a one-call decode.  kv_chunk_size > 0: those chunks.  0:
+// proportional blocks (matrix-core path, two or more state slots per sequence),
+// one workgroup per compute unit (all of them streaming at once, none holding two
+// while another idles): the ranges are whole rounds of one workgroup per compute
+// unit, one round when the batch is at most half of one, else enough rounds that
+// at least half a round is left to share out by key count; elsewhere the smallest
+// fixed chunk the slots allow.
+sa_status_t decode_plan(sa_dtype_t dtype, int32_t batch, int32_t hq, int32_t hkv,
+                        int32_t max_seqlen_k, int32_t kv_chunk_size, int32_t max_num_chunks,
+                        sa::DecodePlan* plan) {
+    if (kv_chunk_size > 0) {
+        *plan = sa::DecodePlan{kv_chunk_size, 0, max_seqlen_k, max_num_chunks};
+        return SA_OK;
+    }
+    if (dtype == SA_BF16 && sa::mfma_decode_supported(hq / hkv) && max_num_chunks >= 2) {
+        const int head_blocks = sa::mfma_decode_head_blocks(hq, hkv);
+        const int per_round = std::max(1, compute_units() / head_blocks);
+        const int64_t ranges = (int64_t)per_round * ((batch + per_round / 2 + per_round - 1) / per_round);
+        sa_status_t s = check_grid(ranges * head_blocks, 512, "sink_attn_decode");
+        if (s != SA_OK) return s;
+        *plan = sa::DecodePlan{0, (int)ranges, max_seqlen_k, max_num_chunks};
+        return SA_OK;
+    }
+    const int32_t chunk = std::max<int32_t>(1, max_seqlen_k / max_num_chunks + (max_seqlen_k % max_num_chunks != 0));
+    sa_status_t s = check_chunk_span(chunk, max_num_chunks, "sink_attn_decode");
+    if (s != SA_OK) return s;
+    if (dtype == SA_BF16 && sa::mfma_decode_supported(hq / hkv) &&
+        (s = check_grid((int64_t)batch * max_num_chunks * ((hq + 7) / 8), 512, "sink_attn_decode")) != SA_OK)
+        return s;
+    *plan = sa::DecodePlan{chunk, 0, max_seqlen_k, max_num_chunks};
     return SA_OK;
 }
 
 hipError_t launch_split(sa_dtype_t dtype, const void* q, const void* k, const void* v,
                         const float* sinks, const int32_t* cu_seqlens_k, int32_t batch,
-                        int32_t hq, int32_t hkv, int32_t chunk, int32_t max_num_chunks,
-                        float sm_scale, float* part_m, float* part_d, float* part_acc,
-                        hipStream_t st) {
+                        int32_t hq, int32_t hkv, const sa::DecodePlan& plan, float sm_scale,
+                        float* part_m, float* part_d, float* part_acc, hipStream_t st) {
     if (dtype == SA_BF16 && sa::mfma_decode_supported(hq / hkv))
-        return sa::launch_mfma_decode_split(q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, chunk,
-                                            max_num_chunks, sm_scale, part_m, part_d, part_acc, st);
+        return sa::launch_mfma_decode_plan(q, k, v, sinks, cu_seqlens_k, batch, hq, hkv, plan,
+                                           sm_scale, part_m, part_d, part_acc, st);
+    // the vector-ALU path takes fixed chunks only (decode_plan never gives it ranges)
     return sa::launch_generic_decode_split(dtype == SA_BF16, q, k, v, sinks, cu_seqlens_k, batch,
-                                           hq, hkv, chunk, max_num_chunks, sm_scale, part_m,
+                                           hq, hkv, plan.chunk, plan.max_chunks, sm_scale, part_m,
                                            part_d, part_acc, st);
 }
 
@@ -349,14 +418,14 @@ sa_status_t sink_attn_decode_split(sa_dtype_t dtype, const void* q, const void* 
                                    float* part_d, float* part_acc, void* stream) {
     sa_status_t s = check_split_args(dtype, q, k, v, sinks, cu_seqlens_k, batch, num_q_heads,
                                      num_kv_heads, head_dim, max_seqlen_k, kv_chunk_size,
-                                     max_num_chunks, sm_scale, part_m, part_d, part_acc);
+                                     max_num_chunks, sm_scale, part_m, part_d, part_acc, false);
     if (s != SA_OK) return s;
     if ((s = check_device()) != SA_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if ((s = debug_check_inputs(st, nullptr, cu_seqlens_k, batch, 1, max_seqlen_k, 0, sinks, num_q_heads)) != SA_OK) return s;
+    const sa::DecodePlan plan{kv_chunk_size, 0, max_seqlen_k, max_num_chunks};
     hipError_t e = launch_split(dtype, q, k, v, sinks, cu_seqlens_k, batch, num_q_heads,
-                                num_kv_heads, kv_chunk_size, max_num_chunks, sm_scale, part_m,
-                                part_d, part_acc, st);
+                                num_kv_heads, plan, sm_scale, part_m, part_d, part_acc, st);
     return finish_launch(e, st, "sink_attn_decode_split");
 }
 
@@ -368,18 +437,21 @@ sa_status_t sink_attn_decode(sa_dtype_t dtype, const void* q, const void* k, con
                              void* out, float* lse, void* stream) {
     sa_status_t s = check_split_args(dtype, q, k, v, sinks, cu_seqlens_k, batch, num_q_heads,
                                      num_kv_heads, head_dim, max_seqlen_k, kv_chunk_size,
-                                     max_num_chunks, sm_scale, part_m, part_d, part_acc);
+                                     max_num_chunks, sm_scale, part_m, part_d, part_acc, true);
     if (s != SA_OK) return s;
     if (!out) return fail(SA_EINVAL, "sink_attn_decode: null pointer argument");
     if ((s = check_device()) != SA_OK) return s;
+    sa::DecodePlan plan;
+    if ((s = decode_plan(dtype, batch, num_q_heads, num_kv_heads, max_seqlen_k, kv_chunk_size,
+                         max_num_chunks, &plan)) != SA_OK)
+        return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if ((s = debug_check_inputs(st, nullptr, cu_seqlens_k, batch, 1, max_seqlen_k, 0, sinks, num_q_heads)) != SA_OK) return s;
     hipError_t e = launch_split(dtype, q, k, v, sinks, cu_seqlens_k, batch, num_q_heads,
-                                num_kv_heads, kv_chunk_size, max_num_chunks, sm_scale, part_m,
-                                part_d, part_acc, st);
+                                num_kv_heads, plan, sm_scale, part_m, part_d, part_acc, st);
     if (e == hipSuccess)
-        e = sa::launch_merge(dtype == SA_BF16, part_m, part_d, part_acc, cu_seqlens_k,
-                             kv_chunk_size, max_num_chunks, batch, num_q_heads, out, lse, st);
+        e = sa::launch_merge_plan(dtype == SA_BF16, part_m, part_d, part_acc, cu_seqlens_k, plan,
+                                  batch, num_q_heads, out, lse, st);
     return finish_launch(e, st, "sink_attn_decode");
 }
 
@@ -399,6 +471,7 @@ sa_status_t sink_attn_merge(sa_dtype_t out_dtype, const float* part_m, const flo
     if (head_dim != 64) return fail(SA_EUNSUPPORTED, "head_dim %d is not supported (only 64)", head_dim);
     if (kv_chunk_size < 1) return fail(SA_EINVAL, "kv_chunk_size must be >= 1, got %d", kv_chunk_size);
     if (max_num_chunks < 1) return fail(SA_EINVAL, "max_num_chunks must be >= 1");
+    if ((s = check_chunk_span(kv_chunk_size, max_num_chunks, "sink_attn_merge")) != SA_OK) return s;
     if ((s = check_device()) != SA_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = sa::launch_merge(out_dtype == SA_BF16, part_m, part_d, part_acc, cu_seqlens_k,

@@ -83,6 +83,8 @@ __device__ __forceinline__ void wave_lds_sync() {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-__host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+// ceil(a / b) for a >= 0, b >= 1, without forming a + b - 1 (which overflows for b
+// near INT32_MAX).
+__host__ __device__ constexpr int ceil_div(int a, int b) { return a / b + (a % b != 0); }
 
 }  // namespace sa

@@ -20,6 +20,62 @@ struct StateSlots {
 };
 
 
+// How a one-call decode cuts each sequence's keys into the blocks whose states the
+// merge combines.  chunk > 0: fixed chunks, block c of sequence b = keys
+// [c * chunk, min((c + 1) * chunk, L_b)).  chunk == 0: proportional blocks, the
+// launch's `ranges` workgroups shared out so that every sequence gets one block
+// plus a share of the other ranges - batch ones proportional to its keys
+// (balanced_first_block); sequence b's n_b blocks split its keys evenly, block c
+// = keys [c * C_b, min((c + 1) * C_b, L_b)) with C_b = ceil(L_b / n_b).  Either
+// way a sequence has at most max_chunks blocks (the state slots per (sequence,
+// head)).
+struct DecodePlan {
+    int chunk;
+    int ranges;
+    int max_seqlen_k;
+    int max_chunks;
+};
+
+// Where the state of block c of sequence b, query head h sits in the state buffers:
+// element b * seq + c * block + h * head of part_m / part_d (and that times head_dim
+// in part_acc).  Chunk-major per head, [B, Hq, slots], for fixed chunks (the
+// layout the ABI documents); block-major, [B, slots, Hq], for proportional blocks,
+// so that one workgroup's states for all heads of a block are contiguous.
+struct SlotLayout {
+    int64_t seq, block, head;
+};
+__host__ __device__ inline SlotLayout head_major_slots(int hq, int slots) {
+    return SlotLayout{(int64_t)hq * slots, 1, slots};
+}
+__host__ __device__ inline SlotLayout block_major_slots(int hq, int slots) {
+    return SlotLayout{(int64_t)hq * slots, hq, 1};
+}
+__host__ __device__ inline SlotLayout plan_slots(const DecodePlan& p, int hq) {
+    return p.chunk > 0 ? head_major_slots(hq, p.max_chunks) : block_major_slots(hq, p.max_chunks);
+}
+
+// Proportional blocks: how many of the ranges beyond one per sequence are shared
+// out by key count, for a batch of `total` keys.  At most ranges - batch, and few
+// enough that no sequence of up to max_seqlen_k keys gets more than max_chunks
+// blocks (a sequence of L keys gets at most floor(L * extra / total) + 2).
+__host__ __device__ inline int balanced_extra_blocks(int total, int batch, const DecodePlan& p) {
+    if (total <= 0 || p.max_chunks < 2 || p.ranges <= batch) return 0;
+    int64_t extra = p.ranges - batch;
+    if (p.max_seqlen_k > 0) {
+        const int64_t cap = (int64_t)(p.max_chunks - 2) * total / p.max_seqlen_k;
+        extra = extra < cap ? extra : cap;
+    }
+    return (int)extra;
+}
+
+// Proportional blocks: the first block of sequence b, whose keys start `before`
+// keys after the batch's first key: floor(before * extra / total) + b.  Strictly
+// increasing in b, so every sequence gets at least one block; the batch has
+// extra + batch blocks in all.
+__host__ __device__ inline int balanced_first_block(int before, int b, int total, int extra) {
+    return total > 0 ? (int)((int64_t)before * extra / total) + b : b;
+}
+
 // Vector-ALU kernel, float32 arithmetic; any group size G = hq / hkv <= 64, head_dim 64.
 hipError_t launch_generic_prefill(bool bf16, const void* q, const void* k, const void* v,
                                   const float* sinks, const int32_t* cu_q, const int32_t* cu_k,
@@ -39,6 +95,15 @@ hipError_t launch_generic_decode_split(bool bf16, const void* q, const void* k, 
 
 // bf16 matrix-core kernels, head_dim 64.
 bool mfma_decode_supported(int group);
+// Workgroups per key range of the matrix-core decode (blocks of eight waves, one
+// wave per KV head or per slice of its query heads).
+int mfma_decode_head_blocks(int hq, int hkv);
+// Split pass of a one-call decode under `plan` (fixed chunks or balanced ranges).
+hipError_t launch_mfma_decode_plan(const void* q, const void* k, const void* v,
+                                   const float* sinks, const int32_t* cu_k, int batch, int hq,
+                                   int hkv, const DecodePlan& plan, float sm_scale,
+                                   float* part_m, float* part_d, float* part_acc,
+                                   hipStream_t stream);
 hipError_t launch_mfma_decode_split(const void* q, const void* k, const void* v,
                                     const float* sinks, const int32_t* cu_k, int batch, int hq,
                                     int hkv, int chunk, int max_chunks, float sm_scale,
@@ -74,6 +139,10 @@ hipError_t launch_qkv_rope(const void* qkv, const void* bias, const int32_t* pos
 hipError_t launch_merge(bool out_bf16, const float* part_m, const float* part_d,
                         const float* part_acc, const int32_t* cu_k, int chunk, int max_chunks,
                         int batch, int hq, void* out, float* lse, hipStream_t stream);
+// The merge of a one-call decode under `plan`.
+hipError_t launch_merge_plan(bool out_bf16, const float* part_m, const float* part_d,
+                             const float* part_acc, const int32_t* cu_k, const DecodePlan& plan,
+                             int batch, int hq, void* out, float* lse, hipStream_t stream);
 
 // One nontemporal 16-byte-load pass over `bytes` (a multiple of 16) of buf by
 // num_blocks workgroups of 512 threads; out[block] = XOR of the 32-bit words the

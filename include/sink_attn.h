@@ -109,7 +109,8 @@ sa_status_t sink_attn_prefill(sa_dtype_t dtype, const void *q, const void *k, co
  *   q          [batch, Hq, D] dtype
  *   k, v       [total_k, Hkv, D] dtype, sequence b's keys at rows [cu_seqlens_k[b], cu_seqlens_k[b+1])
  *   max_seqlen_k  host-side upper bound of L_b
- *   max_num_chunks  slots per (b, h) in the partial buffers; must be >= ceil(max_seqlen_k / C)
+ *   max_num_chunks  slots per (b, h) in the partial buffers; must be >= ceil(max_seqlen_k / C),
+ *                   and max_num_chunks * C must stay below 2^31 (SA_EINVAL otherwise)
  *   part_m, part_d  [batch, Hq, max_num_chunks] float32
  *   part_acc        [batch, Hq, max_num_chunks, D] float32
  * For every c < nchunks(b) the call writes the state after chunk c's keys:
@@ -142,14 +143,33 @@ sa_status_t sink_attn_merge(sa_dtype_t out_dtype, const float *part_m, const flo
                             void *stream);
 
 /*
- * Split-KV decode in one call: sink_attn_decode_split then sink_attn_merge,
- * enqueued back to back on `stream` (same arguments, same partial states, same
- * result as calling the two).
+ * Split-KV decode in one call: a split pass then the log-sum-exp merge, enqueued
+ * back to back on `stream`.  The section splits each sequence's keys into blocks
+ * along the KV length, the sink entering the first block only; the result does not
+ * depend on where the blocks fall.
  *
- *   part_m, part_d, part_acc  caller-owned workspace, laid out as for
- *             sink_attn_decode_split (they hold the chunk states after the call).
+ *   kv_chunk_size > 0  fixed chunks: exactly sink_attn_decode_split followed by
+ *             sink_attn_merge (same arguments, same partial states, same result),
+ *             and the same bounds on max_num_chunks.
+ *   kv_chunk_size == 0 proportional blocks, chosen by the library so that one
+ *             launch gives every compute unit about the same number of key bytes:
+ *             each sequence gets at least one block and the remaining blocks of the
+ *             launch in proportion to its key count, and splits its keys evenly
+ *             over them (contiguous blocks, the first one holding key 0 and the
+ *             sink).  At most max_num_chunks (>= 1) blocks per sequence; more slots
+ *             allow a finer balance (a sequence can be given up to the compute-unit
+ *             count plus one blocks; with max_num_chunks = 1 every sequence is one
+ *             block).  bf16 inputs only; for float32 inputs this picks the smallest
+ *             fixed chunk the slots allow.
+ *   part_m, part_d, part_acc  caller-owned workspace of max_num_chunks state slots
+ *             per (sequence, head): [batch, Hq, max_num_chunks] and
+ *             [batch, Hq, max_num_chunks, D] float32 in size.  With fixed chunks
+ *             they hold the chunk states after the call, laid out as for
+ *             sink_attn_decode_split; with proportional blocks their content and
+ *             layout are the library's own.
  *   out       [batch, Hq, D] dtype;  lse nullable [batch, Hq] float32.
- * Errors: those of sink_attn_decode_split, and SA_EINVAL for a null `out`.
+ * Errors: those of sink_attn_decode_split (kv_chunk_size >= 0 here), and SA_EINVAL
+ * for a null `out` or max_num_chunks < 1.
  */
 sa_status_t sink_attn_decode(sa_dtype_t dtype, const void *q, const void *k, const void *v,
                              const float *sinks, const int32_t *cu_seqlens_k, int32_t batch,
@@ -172,7 +192,8 @@ sa_status_t sink_attn_decode(sa_dtype_t dtype, const void *q, const void *k, con
  * visible).  m is in natural-log units, acc is unnormalised.
  *
  *   Arguments as for sink_attn_prefill, plus kv_chunk_size >= 1 and
- *   max_num_chunks >= ceil(max_seqlen_k / kv_chunk_size) (>= 1).
+ *   max_num_chunks >= ceil(max_seqlen_k / kv_chunk_size) (>= 1), with
+ *   max_num_chunks * kv_chunk_size below 2^31.
  *   part_m, part_d  [total_q, Hq, max_num_chunks] float32 (caller-owned)
  *   part_acc        [total_q, Hq, max_num_chunks, D] float32 (caller-owned)
  * Errors as for sink_attn_prefill; SA_EINVAL for a too small max_num_chunks or a

@@ -126,12 +126,15 @@ def test_prefill_rejects(lib, kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(pa=NULL), sa.SA_EINVAL),
-    (dict(chunk=0), sa.SA_EINVAL),
+    (dict(chunk=0), sa.SA_EINVAL),            # proportional blocks: the one-call decode only
     (dict(max_chunks=7), sa.SA_EINVAL),       # ceil(4096 / 512) = 8 slots needed
     (dict(max_k=-1), sa.SA_EINVAL),
     (dict(hq=64, hkv=7), sa.SA_EINVAL),
     (dict(d=32), sa.SA_EUNSUPPORTED),
     (dict(scale=float("inf")), sa.SA_EINVAL),
+    # chunk c starts at c * chunk in 32 bits: max_num_chunks * chunk must stay below 2^31
+    (dict(chunk=1 << 20, max_chunks=2049, max_k=4096), sa.SA_EINVAL),
+    (dict(chunk=0x7FFFFFFF, max_chunks=2, max_k=4096), sa.SA_EINVAL),
 ])
 def test_decode_split_rejects(lib, kw, status):
     assert _split(lib, **kw) == status
@@ -144,6 +147,9 @@ def test_decode_split_rejects(lib, kw, status):
     (dict(max_chunks=7), sa.SA_EINVAL),
     (dict(hq=64, hkv=5), sa.SA_EINVAL),
     (dict(d=96), sa.SA_EUNSUPPORTED),
+    (dict(chunk=-1), sa.SA_EINVAL),
+    (dict(chunk=0, max_chunks=0), sa.SA_EINVAL),        # proportional blocks need a slot
+    (dict(chunk=1 << 20, max_chunks=2048, max_k=4096), sa.SA_EINVAL),  # chunk span past 2^31
 ])
 def test_decode_rejects(lib, kw, status):
     assert _decode(lib, **kw) == status
@@ -156,6 +162,7 @@ def test_decode_rejects(lib, kw, status):
     (dict(max_chunks=0), sa.SA_EINVAL),
     (dict(batch=0), sa.SA_EINVAL),
     (dict(d=80), sa.SA_EUNSUPPORTED),
+    (dict(chunk=1 << 28, max_chunks=8), sa.SA_EINVAL),  # chunk span past 2^31
 ])
 def test_merge_rejects(lib, kw, status):
     assert _merge(lib, **kw) == status
@@ -173,6 +180,11 @@ def test_valid_call_without_device_reports_launch_error(lib):
     assert _split(lib) == sa.SA_ELAUNCH
     assert _merge(lib) == sa.SA_ELAUNCH
     assert _decode(lib) == sa.SA_ELAUNCH
+    # proportional blocks (chunk 0) pass validation with any slot count >= 1
+    assert _decode(lib, chunk=0, max_chunks=1) == sa.SA_ELAUNCH
+    assert _decode(lib, chunk=0, max_chunks=300) == sa.SA_ELAUNCH
+    # the largest chunk span that fits: 2^31 - 1 keys in one chunk
+    assert _split(lib, chunk=0x7FFFFFFF, max_chunks=1, max_k=4096) == sa.SA_ELAUNCH
 
 
 def test_missing_library_fails_loudly(tmp_path):
@@ -207,6 +219,9 @@ def test_product_does_not_touch_the_oracle():
     (dict(d=80), sa.SA_EUNSUPPORTED),
     (dict(scale=0.0), sa.SA_EINVAL),
     (dict(dtype=sa.SA_FP32, batch=3000, max_chunks=40, max_k=40960), sa.SA_EINVAL),  # generic grid
+    # chunk c starts at c * chunk in 32 bits: an over-provisioned chunk count whose
+    # last chunk would start past 2^31 is refused (2049 slots of 2^20 keys)
+    (dict(chunk=1 << 20, max_chunks=2049, max_k=4096), sa.SA_EINVAL),
 ])
 def test_prefill_split_rejects(lib, kw, status):
     assert _prefill_split(lib, **kw) == status

@@ -23,7 +23,7 @@ SA_FP32, SA_BF16 = 0, 1
 EXPORTS = ("sink_attn_prefill", "sink_attn_decode_split", "sink_attn_merge",
            "sink_attn_decode", "sink_attn_prefill_split", "sink_attn_merge_rows",
            "sink_attn_last_error", "moe_topk_softmax", "qkv_bias_rope",
-           "sink_attn_prefill_state", "sink_attn_read_probe")
+           "sink_attn_prefill_state", "sink_attn_read_probe", "sink_attn_decode_noalloc")
 
 
 class SinkAttnError(RuntimeError):
@@ -59,6 +59,9 @@ def load_library():
     lib.sink_attn_merge.restype = ctypes.c_int
     lib.sink_attn_merge.argtypes = [ctypes.c_int, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp,
                                     vp, vp]
+    lib.sink_attn_decode_noalloc.restype = ctypes.c_int
+    lib.sink_attn_decode_noalloc.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                             i32, f32, vp, vp, vp]
     lib.sink_attn_decode.restype = ctypes.c_int
     lib.sink_attn_decode.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                      i32, i32, f32, vp, vp, vp, vp, vp, vp]
@@ -442,6 +445,37 @@ def decode(q, k, v, sinks, cu_seqlens_k, max_seqlen_k, kv_chunk_size, sm_scale,
                                 int(max_seqlen_k), int(kv_chunk_size), int(max_num_chunks),
                                 float(sm_scale), _ptr(pm), _ptr(pd), _ptr(pa),
                                 _ptr(out), _ptr(lse), _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def decode_noalloc(q, k, v, sinks, cu_seqlens_k, max_seqlen_k, sm_scale, out=None, lse=None,
+                   return_lse=False, stream=None):
+    """``sink_attn_decode_noalloc``: the proportional-block decode with its states in the
+    library's fixed per-device array (no workspace; the library call allocates nothing).
+    Pass ``out`` (and ``lse``) to keep this call free of allocations on the torch side too."""
+    torch = _torch()
+    _check_qkv(q, k, v, sinks)
+    _check_cu(cu_seqlens_k, "cu_seqlens_k")
+    batch = cu_seqlens_k.numel() - 1
+    if q.shape[0] != batch:
+        raise ValueError("q must be [batch, Hq, D] with batch = len(cu_seqlens_k) - 1")
+    _shape(out, q.shape, "out")
+    _shape(lse, (batch, q.shape[1]), "lse")
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _dev(t, name, q.dtype)
+    _dev(sinks, "sinks", torch.float32)
+    _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    if lse is None and return_lse:
+        lse = torch.empty(batch, q.shape[1], device=q.device, dtype=torch.float32)
+    _dev(lse, "lse", torch.float32)
+    _check(lib.sink_attn_decode_noalloc(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(sinks),
+                                        _ptr(cu_seqlens_k), batch, q.shape[1], k.shape[1],
+                                        q.shape[2], int(max_seqlen_k), float(sm_scale), _ptr(out),
+                                        _ptr(lse), _stream(stream)))
     return (out, lse) if return_lse else out
 
 

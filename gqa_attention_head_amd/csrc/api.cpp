@@ -19,6 +19,9 @@
 #include "sa_measure.h"
 #include "sink_attn.h"
 
+static_assert(SA_DECODE_SCRATCH_BYTES == sa::kDecodeScratchBytes,
+              "the header states the size of the decode state array");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -453,6 +456,57 @@ sa_status_t sink_attn_decode(sa_dtype_t dtype, const void* q, const void* k, con
         e = sa::launch_merge_plan(dtype == SA_BF16, part_m, part_d, part_acc, cu_seqlens_k, plan,
                                   batch, num_q_heads, out, lse, st);
     return finish_launch(e, st, "sink_attn_decode");
+}
+
+sa_status_t sink_attn_decode_noalloc(sa_dtype_t dtype, const void* q, const void* k,
+                                     const void* v, const float* sinks,
+                                     const int32_t* cu_seqlens_k, int32_t batch,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t max_seqlen_k, float sm_scale, void* out, float* lse,
+                                     void* stream) {
+    sa_status_t s;
+    if ((s = check_dtype(dtype)) != SA_OK) return s;
+    if (!q || !k || !v || !sinks || !cu_seqlens_k || !out)
+        return fail(SA_EINVAL, "sink_attn_decode_noalloc: null pointer argument");
+    if ((s = check_heads(batch, num_q_heads, num_kv_heads, head_dim)) != SA_OK) return s;
+    if (max_seqlen_k < 0) return fail(SA_EINVAL, "max_seqlen_k must be >= 0");
+    if (!(std::isfinite(sm_scale) && sm_scale > 0.0f))
+        return fail(SA_EINVAL, "sm_scale must be finite and > 0");
+    // State slots per (sequence, head) in the fixed array: acc [pairs * slots * D] floats,
+    // then m and d, each padded to 256 bytes.
+    const int64_t pairs = (int64_t)batch * num_q_heads;
+    const int64_t floats = (int64_t)(sa::kDecodeScratchBytes / sizeof(float));
+    const int64_t fit = (floats - 128) / (pairs * (head_dim + 2));
+    if (fit < 1)
+        return fail(SA_EINVAL,
+                    "sink_attn_decode_noalloc: batch * num_q_heads = %lld needs more than the "
+                    "%zu-byte state array (at most %lld)", (long long)pairs,
+                    sa::kDecodeScratchBytes, (long long)((floats - 128) / (head_dim + 2)));
+    if ((s = check_device()) != SA_OK) return s;
+    // as many slots as one sequence can be given (blocks beyond one per sequence, plus two)
+    const int units = compute_units();
+    const int64_t ranges = (int64_t)units * ((batch + units / 2 + units - 1) / units);
+    const int32_t slots = (int32_t)std::max<int64_t>(1, std::min(ranges - batch + 2, fit));
+    sa::DecodePlan plan;
+    if ((s = decode_plan(dtype, batch, num_q_heads, num_kv_heads, max_seqlen_k, 0, slots,
+                         &plan)) != SA_OK)
+        return s;
+    float* base = nullptr;
+    hipError_t e = sa::decode_scratch(&base);
+    if (e != hipSuccess)
+        return fail(SA_ELAUNCH, "sink_attn_decode_noalloc: state array: %s", hipGetErrorString(e));
+    const int64_t states = pairs * slots;
+    float* part_acc = base;
+    float* part_m = part_acc + states * head_dim;
+    float* part_d = part_m + (states + 63) / 64 * 64;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((s = debug_check_inputs(st, nullptr, cu_seqlens_k, batch, 1, max_seqlen_k, 0, sinks, num_q_heads)) != SA_OK) return s;
+    e = launch_split(dtype, q, k, v, sinks, cu_seqlens_k, batch, num_q_heads, num_kv_heads, plan,
+                     sm_scale, part_m, part_d, part_acc, st);
+    if (e == hipSuccess)
+        e = sa::launch_merge_plan(dtype == SA_BF16, part_m, part_d, part_acc, cu_seqlens_k, plan,
+                                  batch, num_q_heads, out, lse, st);
+    return finish_launch(e, st, "sink_attn_decode_noalloc");
 }
 
 sa_status_t sink_attn_merge(sa_dtype_t out_dtype, const float* part_m, const float* part_d,

@@ -144,6 +144,11 @@ hipError_t launch_merge_plan(bool out_bf16, const float* part_m, const float* pa
                              const float* part_acc, const int32_t* cu_k, const DecodePlan& plan,
                              int batch, int hq, void* out, float* lse, hipStream_t stream);
 
+// Bytes of the fixed per-device state array of sink_attn_decode_noalloc, and its
+// address on the current device (looked up once per device, with it current).
+constexpr size_t kDecodeScratchBytes = size_t(128) << 20;
+hipError_t decode_scratch(float** ptr);
+
 // One nontemporal 16-byte-load pass over `bytes` (a multiple of 16) of buf by
 // num_blocks workgroups of 512 threads; out[block] = XOR of the 32-bit words the
 // workgroup read.

@@ -179,6 +179,33 @@ sa_status_t sink_attn_decode(sa_dtype_t dtype, const void *q, const void *k, con
                              void *out, float *lse, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under graph capture, tight
+ * serving loops, harnesses that forbid allocation): sink_attn_decode with
+ * kv_chunk_size = 0 (proportional blocks), its block states kept in a fixed device
+ * array of SA_DECODE_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends, instead of a caller workspace.  The call itself allocates
+ * nothing: no hipMalloc, no hipFree.
+ *
+ *   Arguments and result as for sink_attn_decode; the library chooses the state
+ *   slots per sequence (as many as fit in the array, up to the most one sequence
+ *   can be given).
+ * Limit: batch * num_q_heads * (head_dim + 2) * 4 bytes (one slot per sequence and
+ * head) must fit in the array: at most 508,398 (sequence, head) pairs at head_dim
+ * 64; beyond it SA_EINVAL, before anything is launched.
+ * Every call on one GPU shares that GPU's array and leaves its states there; no
+ * call needs it cleared.  Calls that overlap on one GPU (on different streams, or
+ * from several host threads) race on it: order them on one stream.  The first call
+ * on a device looks up the array's address on that device.
+ */
+#define SA_DECODE_SCRATCH_BYTES (128u << 20)
+sa_status_t sink_attn_decode_noalloc(sa_dtype_t dtype, const void *q, const void *k,
+                                     const void *v, const float *sinks,
+                                     const int32_t *cu_seqlens_k, int32_t batch,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t max_seqlen_k, float sm_scale, void *out, float *lse,
+                                     void *stream);
+
+/*
  * Split-KV prefill, first pass: the prefill problem of sink_attn_prefill with the
  * keys of every sequence cut into chunks of kv_chunk_size keys, chunk c covering
  * keys [c*C, min((c+1)*C, L_k)) -- the split along the KV length of "GPT-OSS on

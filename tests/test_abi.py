@@ -354,3 +354,35 @@ def _probe(lib, **kw):
 def test_read_probe_rejects(lib, kw, status):
     assert _probe(lib, **kw) == status
     assert lib.sink_attn_read_probe is not None and lib.sink_attn_last_error().decode()
+
+
+def _noalloc(lib, **kw):
+    a = dict(dtype=sa.SA_BF16, q=P, k=P, v=P, sinks=P, cu_k=P, batch=2, hq=64, hkv=8, d=64,
+             max_k=4096, scale=0.125, out=P, lse=NULL, stream=NULL)
+    a.update(kw)
+    return lib.sink_attn_decode_noalloc(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), sa.SA_EINVAL),
+    (dict(out=NULL), sa.SA_EINVAL),
+    (dict(cu_k=NULL), sa.SA_EINVAL),
+    (dict(max_k=-1), sa.SA_EINVAL),
+    (dict(hq=64, hkv=6), sa.SA_EINVAL),
+    (dict(d=128), sa.SA_EUNSUPPORTED),
+    (dict(scale=0.0), sa.SA_EINVAL),
+    # one state slot per (sequence, head) must fit in the fixed array
+    (dict(batch=65535, hq=64, hkv=8), sa.SA_EINVAL),
+])
+def test_decode_noalloc_rejects(lib, kw, status):
+    assert _noalloc(lib, **kw) == status
+    assert lib.sink_attn_last_error().decode()
+
+
+def test_decode_noalloc_limit_is_the_stated_one(lib):
+    """508,398 (sequence, head) pairs fit at head_dim 64 (the header's figure); one more
+    pair does not."""
+    if _no_gpu():
+        assert _noalloc(lib, batch=63549, hq=8, hkv=8) == sa.SA_ELAUNCH      # 508,392 pairs
+    assert _noalloc(lib, batch=63550, hq=8, hkv=8) == sa.SA_EINVAL        # 508,400 pairs
+    assert "state array" in lib.sink_attn_last_error().decode()

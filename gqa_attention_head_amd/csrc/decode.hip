@@ -368,15 +368,6 @@ hipError_t launch_g(const void* q, const void* k, const void* v, const float* si
 
 }  // namespace
 
-bool mfma_decode_supported(int group) { return group >= 1 && group <= 64; }
-
-int mfma_decode_head_blocks(int hq, int hkv) {
-    const int group = hq / hkv;
-    int slice = group;  // query heads per wave
-    if (group > 16) slice = group % 16 == 0 ? 16 : group % 8 == 0 ? 8 : group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1;
-    return ceil_div(hkv * (group / slice), 8);
-}
-
 hipError_t launch_mfma_decode_plan(const void* q, const void* k, const void* v,
                                    const float* sinks, const int32_t* cu_k, int batch, int hq,
                                    int hkv, const DecodePlan& plan, float sm_scale,

@@ -395,8 +395,6 @@ hipError_t dispatch(const void* q, const void* k, const void* v, const float* si
 
 }  // namespace
 
-bool mfma_prefill_supported(int group) { return group >= 1 && group <= 64; }
-
 hipError_t launch_mfma_prefill(const void* q, const void* k, const void* v, const float* sinks,
                                const int32_t* cu_q, const int32_t* cu_k, int batch, int hq,
                                int hkv, int max_lq, int max_lk, float sm_scale, int causal,

@@ -194,11 +194,6 @@ hipError_t launch_experts(const void* logits, int64_t num_tokens, int k, int32_t
 
 }  // namespace
 
-bool topk_softmax_supported(int num_experts) {
-    return num_experts == 8 || num_experts == 16 || num_experts == 32 || num_experts == 64 ||
-           num_experts == 128 || num_experts == 256 || num_experts == 512;
-}
-
 hipError_t launch_topk_softmax(const void* logits, int64_t num_tokens, int num_experts, int k,
                                int32_t* indices, void* weights, hipStream_t stream) {
     switch (num_experts) {

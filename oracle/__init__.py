@@ -145,8 +145,14 @@ _DEFAULT = None
 
 
 def default(rebuild: bool = False) -> Oracle:
-    """The oracle built from ``oracle.c`` next to this file (compiled on first use)."""
+    """The oracle built from ``oracle.c`` next to this file (compiled on first use), or
+    the library that SINK_ATTN_ORACLE_LIBRARY names (the sanitizer build of the tests)."""
     global _DEFAULT
+    override = os.environ.get("SINK_ATTN_ORACLE_LIBRARY")
+    if override:
+        if _DEFAULT is None or _DEFAULT.path != override:
+            _DEFAULT = Oracle(override)
+        return _DEFAULT
     if _DEFAULT is None or rebuild:
         if rebuild or not os.path.exists(LIBRARY) or \
                 os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):

@@ -2,17 +2,24 @@
 """Benchmark of grouped-query attention with per-head sinks on one MI355X.
 
 One step = one split-KV decode call (split pass, then the log-sum-exp merge,
-enqueued back to back on the stream) of the batched gpt-oss-shaped decode workload: 32 sequences x 1 query token over 4096 cached
-keys, 64 query heads on 8 KV heads, head_dim 64, bf16, 8 KV chunks per
-sequence.  `value` is the K/V bytes that step reads (268,435,456 B) divided by
-the step time, in GB/s; inputs are resident in HBM before timing starts and
-the timed steps rotate over several copies of K/V (>= 1 GiB in total) so the
+enqueued back to back on the stream) of the batched gpt-oss-shaped decode
+workload: 32 sequences x 1 query token over 4096 cached keys, 64 query heads on
+8 KV heads, head_dim 64, bf16, 8 KV chunks of 512 keys per sequence.  `value` is
+the K/V bytes that step reads (268,435,456 B) divided by the step's GPU time, in
+GB/s: the timed steps are bracketed by a synchronisation on both sides, and an
+event pair on the launch stream around their back-to-back launches gives the GPU
+time (the host clock's figure for the same bracket is `wall_ms_per_step`).  Each
+step is a call prepared once (arguments checked and marshalled), the warm-up runs
+at least 100 steps and 200 ms, inputs are resident in HBM before timing starts,
+and the steps rotate over several copies of K/V (>= 1 GiB in total) so the
 256 MB last-level cache cannot serve repeats.
 
 The same JSON line carries the prefill half of the metric (causal prefill,
 4 x 4096 tokens, 64/8 heads, bf16) as achieved TFLOP/s over the causal pairs,
 the roofline of the dominant kernel (timed with HIP events on the stream it
-runs on) and the fp64 CPU oracle timed on the host on a bounded sample.
+runs on), the other workloads (tiny fp32 prefill, long-context ragged decode,
+mixed packed batch with each part against its own roofline) and the fp64 CPU
+oracle timed on the host on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -57,7 +64,15 @@ def _sync():
     torch.cuda.synchronize()
 
 
+def _events():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
 def bench_decode(steps: int, warmup: int):
+    """The headline step: one sink_attn_decode call (split pass + merge) on the batched
+    decode workload, each call prepared once (arguments checked and marshalled) so the
+    host issues steps faster than the GPU runs them."""
     import torch
     import gqa_attention_head_amd as sa
     from gqa_attention_head_amd import workloads as W
@@ -80,46 +95,51 @@ def bench_decode(steps: int, warmup: int):
     ws = sa.DecodeWorkspace(wl.batch, wl.num_q_heads, nch, wl.head_dim, dev)
     out = torch.empty(wl.batch, wl.num_q_heads, wl.head_dim, device=dev, dtype=torch.bfloat16)
     lse = torch.empty(wl.batch, wl.num_q_heads, device=dev, dtype=torch.float32)
+    calls = [sa.prepare_decode(q, ks[j], vs[j], sinks, cu_k, max_lk, chunk, wl.sm_scale, ws, out,
+                               lse) for j in range(KV_COPIES)]
 
     def step(i):
-        j = i % KV_COPIES
-        sa.decode(q, ks[j], vs[j], sinks, cu_k, max_lk, chunk, wl.sm_scale, workspace=ws,
-                  out=out, lse=lse)
+        calls[i % KV_COPIES]()
 
-    for i in range(warmup):
-        step(i)
+    # The clocks need some tens of milliseconds of load to settle after idle or a
+    # change of load: at least 100 steps and 200 ms of warm-up.
+    warm_up(step, max(warmup, 100), 200.0)
+    # The timed steps, bracketed by a synchronisation on both sides; their GPU time
+    # comes from an event pair on the launch stream around the back-to-back launches,
+    # the host clock gives the wall time of the same bracket.
+    e0, e1 = _events()
     _sync()
-    # Average launch duration of the step's dominant kernel (the split pass), with
-    # events on the stream it runs on, over a run of back-to-back launches (the
-    # call sa.decode makes first); an event pair around every single launch would
-    # add its own gap to each.
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    ev[0].record()
+    t0 = time.perf_counter()
+    e0.record()
     for i in range(steps):
+        step(i)
+    e1.record()
+    _sync()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ms_per_step = e0.elapsed_time(e1) / steps
+    # Average launch duration of the step's dominant kernel (the split pass), with
+    # events on the stream it runs on, over a run of back-to-back launches.
+    split_steps = max(steps, 200)
+    warm_up(lambda i: sa.decode_split(q, ks[i % KV_COPIES], vs[i % KV_COPIES], sinks, cu_k, max_lk,
+                                      chunk, nch, wl.sm_scale, partials=ws.partials), 50, 60.0)
+    e0.record()
+    for i in range(split_steps):
         j = i % KV_COPIES
         sa.decode_split(q, ks[j], vs[j], sinks, cu_k, max_lk, chunk, nch, wl.sm_scale,
                         partials=ws.partials)
-    ev[1].record()
+    e1.record()
     _sync()
-    split_ms = ev[0].elapsed_time(ev[1]) / steps
-    # the timed steps: nothing between the launches
-    _sync()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(i)
-    _sync()
-    wall2 = time.perf_counter() - t0
+    split_ms = e0.elapsed_time(e1) / split_steps
     # The same step replayed from captured HIP graphs (one per K/V copy).
     graphs = [sa.DecodeGraph(q, ks[j], vs[j], sinks, cu_k, max_lk, chunk, wl.sm_scale, out=out,
                              lse=lse) for j in range(KV_COPIES)]
-    for i in range(warmup):
-        graphs[i % KV_COPIES].replay()
-    _sync()
-    t0 = time.perf_counter()
+    warm_up(lambda i: graphs[i % KV_COPIES].replay(), max(warmup, 100), 200.0)
+    e0.record()
     for i in range(steps):
         graphs[i % KV_COPIES].replay()
+    e1.record()
     _sync()
-    graph_ms = (time.perf_counter() - t0) * 1e3 / steps
+    graph_ms = e0.elapsed_time(e1) / steps
     # one step at a time, the host waiting for each (a serving loop that needs the
     # result before the next step): eager launches against the captured graph
     sync_ms = {}
@@ -133,21 +153,60 @@ def bench_decode(steps: int, warmup: int):
             torch.cuda.synchronize()
         sync_ms[name] = (time.perf_counter() - t0) * 1e3 / steps
     # distribution of single steps (an event pair around each step adds its own gap)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    warm_up(step, 100, 100.0)
+    evs = [_events() for _ in range(steps)]
     for i in range(steps):
         evs[i][0].record()
         step(i)
         evs[i][1].record()
     _sync()
-    step_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    step_ms = np.array([a.elapsed_time(b) for a, b in evs])
     kv_bytes = wl.kv_bytes()
-    ms_per_step = wall2 * 1e3 / steps
     return dict(
-        workload=wl.name, kv_bytes=kv_bytes, ms_per_step=ms_per_step,
+        workload=wl.name, kv_bytes=kv_bytes, ms_per_step=ms_per_step, wall_ms_per_step=wall_ms,
         gbs=kv_bytes / (ms_per_step * 1e-3) / 1e9,
         split_ms_mean=float(split_ms), graph_ms_per_step=graph_ms, sync_ms=sync_ms,
         step_ms_p10_p50_p90=[float(np.percentile(step_ms, q)) for q in (10, 50, 90)],
         batch=wl.batch, kv_len=int(max_lk), chunk=chunk, num_chunks=nch, wl=wl)
+
+
+def bench_tiny_prefill(steps: int = 400):
+    """The tiny fp32 causal prefill (1 x 128 tokens, 4 query heads on 1 KV head): launch
+    latency bound, so its time is reported two ways: back-to-back calls (GPU time per
+    call, from an event pair) and one call at a time with the host waiting for each."""
+    import torch
+    import gqa_attention_head_amd as sa
+    from gqa_attention_head_amd import workloads as W
+
+    wl = W.tiny_prefill_fp32()
+    dev = torch.device("cuda", 0)
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in (wl.q32, wl.k32, wl.v32))
+    sinks = torch.from_numpy(wl.sinks).to(dev)
+    cu_q, cu_k = torch.from_numpy(wl.cu_q).to(dev), torch.from_numpy(wl.cu_k).to(dev)
+    out = torch.empty_like(q)
+    lq = int(wl.seqlens_q.max())
+    call = sa.prepare_prefill(q, k, v, sinks, cu_q, cu_k, lq, lq, wl.sm_scale, out, causal=True)
+    warm_up(lambda i: call(), 100, 60.0)
+    e0, e1 = _events()
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    _sync()
+    gpu_ms = e0.elapsed_time(e1) / steps
+    for _ in range(20):
+        call()
+        torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+        torch.cuda.synchronize()
+    synced_ms = (time.perf_counter() - t0) * 1e3 / steps
+    return {"workload": "tiny_prefill_fp32_b1_s128_hq4_hkv1_d64", "dtype": "f32",
+            "ms_back_to_back": round(gpu_ms, 5), "ms_host_synced": round(synced_ms, 5),
+            "flops": wl.prefill_flops(),
+            "note": "launch-latency bound: time only; parity is checked in the CPU baseline leg and the tests",
+            "_out": out.cpu().numpy(), "_wl": wl}
 
 
 def bench_prefill(steps: int, warmup: int):
@@ -355,11 +414,26 @@ def _time_ms(fn, steps: int, warmup: int) -> float:
     return e0.elapsed_time(e1) / steps
 
 
-def bench_ragged_decode(steps: int = 30, warmup: int = 10):
+def _time_calls(calls, steps: int, warmup: int, min_ms: float = 60.0) -> float:
+    """Mean GPU time of one call, from an event pair around `steps` back-to-back calls
+    that rotate over `calls`, after a warm-up of at least `warmup` calls and `min_ms`."""
+    n = len(calls)
+    warm_up(lambda i: calls[i % n](), warmup, min_ms)
+    e0, e1 = _events()
+    e0.record()
+    for i in range(steps):
+        calls[i % n]()
+    e1.record()
+    _sync()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_ragged_decode(steps: int = 40, warmup: int = 20):
     """The long-context ragged decode (8 sequences, KV lengths of the seeded workload, 1024 to
-    131072 keys, 64/8 heads, bf16, chunk 2048): one decode call (split pass + merge) per
-    step.  K/V (1.6 GB, above the last-level cache) are drawn on the device from a seeded
-    generator: the values do not change the timing, the lengths do."""
+    131072 keys, 64/8 heads, bf16): one decode call (split pass + merge) per step, with the
+    configured 2048-key chunks and with proportional blocks (kv_chunk_size 0: one
+    workgroup per compute unit).  K/V (1.6 GB, above the last-level cache) are drawn on the
+    device from a seeded generator: the values do not change the timing, the lengths do."""
     import torch
     import gqa_attention_head_amd as sa
     from gqa_attention_head_amd import workloads as W
@@ -376,25 +450,38 @@ def bench_ragged_decode(steps: int = 30, warmup: int = 10):
     sinks = 2.0 * torch.randn(hq, device=dev, generator=g)
     cu_k = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
     max_k = int(lens.max())
-    nch = -(-max_k // chunk)
-    ws = sa.DecodeWorkspace(len(lens), hq, nch, d, dev)
     out = torch.empty_like(q)
-    ms = _time_ms(lambda: sa.decode(q, k, v, sinks, cu_k, max_k, chunk, 0.125, workspace=ws, out=out),
-                  steps, warmup)
     kv_bytes = total * hkv * d * 2 * 2
+    res = {"workload": f"ragged_decode_bf16_b{len(lens)}_kv1024-131072_h64g8_d64",
+           "kv_lengths": [int(x) for x in lens], "kv_bytes": kv_bytes}
+    for name, c, slots in (("fixed_chunk_2048", chunk, -(-max_k // chunk)),
+                           ("proportional_blocks", 0, sa.balanced_slots(len(lens), hq, d, dev))):
+        ws = sa.DecodeWorkspace(len(lens), hq, slots, d, dev)
+        ms = _time_calls([sa.prepare_decode(q, k, v, sinks, cu_k, max_k, c, 0.125, ws, out)],
+                         steps, warmup)
+        gbs = kv_bytes / (ms * 1e-3) / 1e9
+        res[name] = {"kv_chunk_size": c, "slots": slots, "ms": round(ms, 4),
+                     "value": round(gbs, 2), "unit": "GB/s", "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    best = res["proportional_blocks"]
+    res.update(ms=best["ms"], value=best["value"], unit="GB/s", hbm_frac=best["hbm_frac"],
+               mode="proportional_blocks")
     del k, v
-    return {"workload": f"ragged_decode_bf16_b{len(lens)}_kv1024-131072_h64g8_d64_chunk{chunk}",
-            "kv_lengths": [int(x) for x in lens], "kv_bytes": kv_bytes, "ms": round(ms, 4),
-            "value": round(kv_bytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
-            "hbm_frac": round(kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return res
 
 
-def bench_mixed_varlen(steps: int = 30, warmup: int = 10):
+MIXED_COPIES = 4  # rotated copies of the mixed batch's K/V (4 x 332 MB)
+
+
+def bench_mixed_varlen(steps: int = 40, warmup: int = 20):
     """The mixed packed batch (4 prefill chunks of 512-2048 new tokens over 0-8192 cached
-    keys, then 12 single-token decodes over 1024-32768 keys, 64/8 heads, bf16), two ways:
-    one prefill call over all 16 sequences, and a prefill call over the 4 chunks plus a
-    decode call (chunk 2048) over the 12 decodes, on one stream or on two.  The roofline time is
-    max(prefill flops / 2.5 PF, decode K/V bytes / 8 TB/s)."""
+    keys, then 12 single-token decodes over 1024-32768 keys, 64/8 heads, bf16).  Each part
+    against its own roofline: the prefill chunks in one prefill call (TFLOP/s over their
+    causal pairs, against 2.5 PF) and the 12 decodes in one decode call (K/V GB/s, against
+    8 TB/s; proportional blocks, and 2048-key chunks for reference).  Then the whole batch:
+    one prefill call over all 16 sequences, the two calls on one stream, and the two calls
+    on two streams, each against max(prefill flops / 2.5 PF, decode bytes / 8 TB/s).  The
+    timed calls rotate over 4 copies of K/V (1.3 GB) so that the last-level cache cannot
+    serve repeats."""
     import torch
     import gqa_attention_head_amd as sa
     from gqa_attention_head_amd import workloads as W
@@ -405,7 +492,10 @@ def bench_mixed_varlen(steps: int = 30, warmup: int = 10):
     def up(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
-    q, k, v = up(wl.q16), up(wl.k16), up(wl.v16)
+    q = up(wl.q16)
+    k0, v0 = up(wl.k16), up(wl.v16)
+    ks = [k0] + [k0.clone() for _ in range(MIXED_COPIES - 1)]
+    vs = [v0] + [v0.clone() for _ in range(MIXED_COPIES - 1)]
     sinks = torch.from_numpy(wl.sinks).to(dev)
     cu_q = torch.from_numpy(wl.cu_q).to(dev)
     cu_k = torch.from_numpy(wl.cu_k).to(dev)
@@ -417,41 +507,63 @@ def bench_mixed_varlen(steps: int = 30, warmup: int = 10):
                     for a, b in zip(lq[:npre], lk[:npre]))
     bytes_dec = int(lk[npre:].sum()) * 8 * 64 * 2 * 2
     r0 = int(wl.cu_q[npre])
-    chunk = 2048
-    nch = -(-int(lk[npre:].max()) // chunk)
-    ws = sa.DecodeWorkspace(len(lq) - npre, 64, nch, 64, dev)
+    ndec = len(lq) - npre
     q_dec, out_dec = q[r0:], out[r0:]
-
-    def one_call():
-        sa.prefill(q, k, v, sinks, cu_q, cu_k, int(lq.max()), int(lk.max()), wl.sm_scale,
-                   causal=True, out=out)
-
-    def two_calls():
-        sa.prefill(q, k, v, sinks, cu_q[:npre + 1], cu_k[:npre + 1], int(lq[:npre].max()),
-                   int(lk[:npre].max()), wl.sm_scale, causal=True, out=out)
-        sa.decode(q_dec, k, v, sinks, cu_k[npre:], int(lk[npre:].max()), chunk, wl.sm_scale,
-                  workspace=ws, out=out_dec)
-
+    cu_pre, cu_kpre, cu_dec = cu_q[:npre + 1], cu_k[:npre + 1], cu_k[npre:]
+    max_q_pre, max_k_pre = int(lq[:npre].max()), int(lk[:npre].max())
+    max_k_dec = int(lk[npre:].max())
+    ws_fixed = sa.DecodeWorkspace(ndec, 64, -(-max_k_dec // 2048), 64, dev)
+    ws_prop = sa.DecodeWorkspace(ndec, 64, sa.balanced_slots(ndec, 64, 64, dev), 64, dev)
+    pre = [sa.prepare_prefill(q, ks[j], vs[j], sinks, cu_pre, cu_kpre, max_q_pre, max_k_pre,
+                              wl.sm_scale, out) for j in range(MIXED_COPIES)]
+    dec = [sa.prepare_decode(q_dec, ks[j], vs[j], sinks, cu_dec, max_k_dec, 0, wl.sm_scale,
+                             ws_prop, out_dec) for j in range(MIXED_COPIES)]
+    dec_fixed = [sa.prepare_decode(q_dec, ks[j], vs[j], sinks, cu_dec, max_k_dec, 2048,
+                                   wl.sm_scale, ws_fixed, out_dec) for j in range(MIXED_COPIES)]
+    one = [sa.prepare_prefill(q, ks[j], vs[j], sinks, cu_q, cu_k, int(lq.max()), int(lk.max()),
+                              wl.sm_scale, out) for j in range(MIXED_COPIES)]
     side = torch.cuda.Stream(device=dev)  # default priority
+    side_dec = []
+    with torch.cuda.stream(side):
+        side_dec = [sa.prepare_decode(q_dec, ks[j], vs[j], sinks, cu_dec, max_k_dec, 0,
+                                      wl.sm_scale, ws_prop, out_dec) for j in range(MIXED_COPIES)]
+    torch.cuda.synchronize()
 
-    def two_streams():
+    def two_calls(j):
+        return lambda: (pre[j](), dec[j]())
+
+    def two_streams(j):
         # the MFMA-bound prefill and the HBM-bound decode overlap on two streams
-        main = torch.cuda.current_stream()
-        side.wait_stream(main)
-        with torch.cuda.stream(side):
-            sa.decode(q_dec, k, v, sinks, cu_k[npre:], int(lk[npre:].max()), chunk, wl.sm_scale,
-                      workspace=ws, out=out_dec)
-        sa.prefill(q, k, v, sinks, cu_q[:npre + 1], cu_k[:npre + 1], int(lq[:npre].max()),
-                   int(lk[:npre].max()), wl.sm_scale, causal=True, out=out)
-        main.wait_stream(side)
+        def run():
+            main = torch.cuda.current_stream()
+            side.wait_stream(main)
+            side_dec[j]()
+            pre[j]()
+            main.wait_stream(side)
+        return run
 
     roof_ms = max(flops_pre / (BF16_PEAK_TFLOPS * 1e12), bytes_dec / (HBM_PEAK_GBS * 1e9)) * 1e3
     res = {"workload": wl.name, "prefill_flops": flops_pre, "decode_kv_bytes": bytes_dec,
-           "roofline_ms": round(roof_ms, 4)}
-    for name, fn in (("one_prefill_call", one_call), ("prefill_plus_decode_calls", two_calls),
-                     ("prefill_and_decode_on_two_streams", two_streams)):
-        ms = _time_ms(fn, steps, warmup)
+           "kv_copies_rotated": MIXED_COPIES, "roofline_ms": round(roof_ms, 4)}
+    ms = _time_calls(pre, steps, warmup)
+    tf = flops_pre / (ms * 1e-3) / 1e12
+    res["prefill_part"] = {"ms": round(ms, 4), "value": round(tf, 2), "unit": "TFLOP/s",
+                           "roofline": {"bound": "mfma", "peak": BF16_PEAK_TFLOPS,
+                                        "frac": round(tf / BF16_PEAK_TFLOPS, 4)}}
+    for name, calls in (("decode_part", dec), ("decode_part_fixed_chunk_2048", dec_fixed)):
+        ms = _time_calls(calls, steps, warmup)
+        gbs = bytes_dec / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "value": round(gbs, 2), "unit": "GB/s",
+                     "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS,
+                                  "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    res["decode_part"]["mode"] = "proportional_blocks"
+    for name, calls in (("one_prefill_call", one),
+                        ("prefill_plus_decode_calls", [two_calls(j) for j in range(MIXED_COPIES)]),
+                        ("prefill_and_decode_on_two_streams",
+                         [two_streams(j) for j in range(MIXED_COPIES)])):
+        ms = _time_calls(calls, steps, warmup)
         res[name] = {"ms": round(ms, 4), "roofline_frac": round(roof_ms / ms, 4)}
+    del ks, vs
     return res
 
 
@@ -527,58 +639,110 @@ def bench_epilogue(steps: int, warmup: int):
                          "algorithmic_bytes": int(nbytes)}}
 
 
-def cpu_baseline(dec_wl, pre_wl, budget_s: float = 20.0):
+def _cpu_threads():
+    """Threads for the oracle: the cores this process may run on (its affinity set),
+    capped by OMP_NUM_THREADS when that is set (the GPU machine sets it to its CPU share)."""
+    n = _affinity()
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    return min(n, int(omp)) if omp.isdigit() and int(omp) > 0 else n
+
+
+def _affinity():
+    return len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+
+
+def _median_rate(run, units: float, rounds: int = 3, min_s: float = 2.0):
+    """Median over `rounds` timing rounds (each repeating `run` for at least `min_s`) of
+    units per second; returns (rate, seconds per run, runs per round)."""
+    rates, per_run, reps = [], [], []
+    for _ in range(rounds):
+        t0 = time.perf_counter()
+        n = 0
+        while True:
+            run()
+            n += 1
+            if time.perf_counter() - t0 >= min_s:
+                break
+        sec = (time.perf_counter() - t0) / n
+        rates.append(units / sec)
+        per_run.append(sec)
+        reps.append(n)
+    i = int(np.argsort(rates)[len(rates) // 2])
+    return rates[i], per_run[i], reps[i]
+
+
+def cpu_baseline(dec_wl, pre_wl, tiny=None):
     """The fp64 oracle, untuned, on the host: decode over whole sequences of the decode
-    workload, prefill over sampled query rows of the prefill workload."""
+    workload, prefill over sampled query rows of the prefill workload, each the median of
+    three timing rounds; and the tiny fp32 prefill's GPU output checked against it."""
     import oracle
     orc = oracle.default()
-    threads = min(16, os.cpu_count() or 1)
+    threads = _cpu_threads()
     # decode: the first 8 of 32 sequences (all 64 heads, all 4096 keys each)
     nseq = 8
     sub_rows = np.arange(nseq, dtype=np.int64)
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        orc.workload(dec_wl, rows=sub_rows, nthreads=threads)
-        reps += 1
-        if time.perf_counter() - t0 > budget_s / 2:
-            break
-    dec_s = (time.perf_counter() - t0) / reps
     dec_bytes = int(dec_wl.seqlens_k[:nseq].sum()) * dec_wl.num_kv_heads * dec_wl.head_dim * 2 * 2
+    dec_rate, dec_s, reps = _median_rate(
+        lambda: orc.workload(dec_wl, rows=sub_rows, nthreads=threads), dec_bytes, min_s=3.0)
     # prefill: 16 rows from the end of each sequence (the longest rows), all heads
     rows = np.concatenate([np.arange(int(pre_wl.cu_q[b + 1]) - 16, int(pre_wl.cu_q[b + 1]))
                            for b in range(pre_wl.batch)]).astype(np.int64)
-    t0 = time.perf_counter()
-    orc.workload(pre_wl, rows=rows, nthreads=threads)
-    pre_s = time.perf_counter() - t0
     pairs = 0
     for r in rows:
         b = int(np.searchsorted(pre_wl.cu_q, r, side="right") - 1)
         i = int(r - pre_wl.cu_q[b])
         pairs += int(pre_wl.seqlens_k[b]) - int(pre_wl.seqlens_q[b]) + i + 1
     pre_flops = 4 * pre_wl.head_dim * pre_wl.num_q_heads * pairs
+    pre_rate, pre_s, pre_reps = _median_rate(
+        lambda: orc.workload(pre_wl, rows=rows, nthreads=threads), pre_flops, min_s=2.0)
     # decode on one thread: the first sequence
-    t0 = time.perf_counter()
-    reps1 = 0
-    while time.perf_counter() - t0 < 2.0:
-        orc.workload(dec_wl, rows=np.arange(1, dtype=np.int64), nthreads=1)
-        reps1 += 1
-    dec1_s = (time.perf_counter() - t0) / reps1
     dec1_bytes = int(dec_wl.seqlens_k[0]) * dec_wl.num_kv_heads * dec_wl.head_dim * 2 * 2
-    return dict(
-        value=dec_bytes / dec_s / 1e9, unit="GB/s", cores=threads, kind="oracle",
+    dec1_rate, dec1_s, dec1_reps = _median_rate(
+        lambda: orc.workload(dec_wl, rows=np.arange(1, dtype=np.int64), nthreads=1), dec1_bytes,
+        min_s=1.0)
+    res = dict(
+        value=dec_rate / 1e9, unit="GB/s", cores=threads, kind="oracle",
         sample=f"decode: {nseq} of {dec_wl.batch} sequences x 64 heads x 4096 keys "
-               f"({dec_bytes} B of K/V), {reps} run(s), {dec_s:.3f} s each",
+               f"({dec_bytes} B of K/V), median of 3 rounds of {reps} run(s), {dec_s:.3f} s each",
+        cores_note=f"{threads} threads: this process's CPU set ({_affinity()} cores) capped by "
+                   f"OMP_NUM_THREADS={os.environ.get('OMP_NUM_THREADS', 'unset')}; "
+                   f"os.cpu_count() = {os.cpu_count()}",
         cpu_model=_cpu_model(),
-        decode_one_thread=dict(value=dec1_bytes / dec1_s / 1e9, unit="GB/s", cores=1,
-                               sample=f"decode: 1 sequence x 64 heads x 4096 keys, {reps1} run(s)"),
-        prefill=dict(value=pre_flops / pre_s / 1e12, unit="TFLOP/s",
-                     sample=f"prefill: {rows.size} query rows (last 16 of each sequence) x 64 heads, "
-                            f"{pre_s:.3f} s"),
+        decode_one_thread=dict(value=dec1_rate / 1e9, unit="GB/s", cores=1,
+                               sample=f"decode: 1 sequence x 64 heads x 4096 keys, median of 3 "
+                                      f"rounds of {dec1_reps} run(s), {dec1_s:.3f} s each"),
+        prefill=dict(value=pre_rate / 1e12, unit="TFLOP/s", cores=threads,
+                     sample=f"prefill: {rows.size} query rows (last 16 of each sequence) x 64 "
+                            f"heads, median of 3 rounds of {pre_reps} run(s), {pre_s:.3f} s each"),
         router=_cpu_router(), qkv_epilogue=_cpu_epilogue())
+    if tiny is not None:
+        wl = tiny["_wl"]
+        t0 = time.perf_counter()
+        ref, _ = orc.workload(wl, nthreads=threads)
+        sec = time.perf_counter() - t0
+        err = float(np.abs(tiny["_out"].astype(np.float64) - ref).max())
+        res["tiny_prefill_fp32"] = dict(seconds=round(sec, 5), gpu_max_abs_err=err,
+                                        tolerance=1e-5, within_tolerance=bool(err <= 1e-5))
+    return res
 
 
 def _cpu_model() -> str:
+    """The host CPU as the kernel names it: lscpu's vendor, model name, family/model/stepping
+    and sockets, else /proc/cpuinfo's model name."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        f = {}
+        for line in out.splitlines():
+            if ":" in line:
+                key, val = line.split(":", 1)
+                f.setdefault(key.strip(), val.strip())
+        if f.get("Model name"):
+            fam = "/".join(f.get(k, "?") for k in ("CPU family", "Model", "Stepping"))
+            return (f"{f.get('Vendor ID', '')} {f['Model name']} (family/model/stepping {fam}, "
+                    f"{f.get('Socket(s)', '?')} socket(s), {f.get('CPU(s)', '?')} logical CPUs)").strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
     try:
         for line in open("/proc/cpuinfo"):
             if line.startswith("model name"):
@@ -670,6 +834,7 @@ def main(argv=None):
     # host-synchronised loops) its two streams no longer overlap in this process.
     mixed = None if args.no_prefill else bench_mixed_varlen()
     dec = bench_decode(args.steps, args.warmup)
+    tiny = None if args.no_prefill else bench_tiny_prefill()
     pre = None if args.no_prefill else bench_prefill(args.prefill_steps, 50)
     long_kv = None if args.no_prefill else bench_prefill_long_kv(max(10, args.prefill_steps // 2), 20)
     groups = None if args.no_prefill else bench_prefill_groups()
@@ -679,7 +844,7 @@ def main(argv=None):
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(dec["wl"], pre["wl"] if pre else __import__(
-            "gqa_attention_head_amd.workloads", fromlist=["x"]).causal_prefill())
+            "gqa_attention_head_amd.workloads", fromlist=["x"]).causal_prefill(), tiny)
 
     kernel_gbs = dec["kv_bytes"] / (dec["split_ms_mean"] * 1e-3) / 1e9
     traffic = measured_traffic()
@@ -692,6 +857,7 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(dec["ms_per_step"], 5),
+        "wall_ms_per_step": round(dec["wall_ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -741,6 +907,8 @@ def main(argv=None):
         line["qkv_epilogue"] = epilogue
     if ragged is not None:
         line["ragged_decode"] = ragged
+    if tiny is not None:
+        line["tiny_prefill_fp32"] = {k: v for k, v in tiny.items() if not k.startswith("_")}
     if mixed is not None:
         line["mixed_varlen"] = mixed
     if cpu is not None:

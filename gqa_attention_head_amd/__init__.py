@@ -479,6 +479,30 @@ def decode_noalloc(q, k, v, sinks, cu_seqlens_k, max_seqlen_k, sm_scale, out=Non
     return (out, lse) if return_lse else out
 
 
+def prepare_prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                    sm_scale, out, causal=True, lse=None, stream=None):
+    """One ``sink_attn_prefill`` call with its arguments checked and marshalled once:
+    returns a function of no arguments that issues the call again (see
+    ``prepare_decode``)."""
+    prefill(q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, sm_scale,
+            causal=causal, out=out, lse=lse, stream=stream)  # checks every argument
+    lib = load_library()
+    args = (_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(sinks), _ptr(cu_seqlens_q),
+            _ptr(cu_seqlens_k), cu_seqlens_q.numel() - 1, q.shape[1], k.shape[1], q.shape[2],
+            int(max_seqlen_q), int(max_seqlen_k), float(sm_scale), int(bool(causal)), _ptr(out),
+            _ptr(lse), _stream(stream))
+    keep = (q, k, v, sinks, cu_seqlens_q, cu_seqlens_k, out, lse)
+    fn = lib.sink_attn_prefill
+
+    def call():
+        status = fn(*args)
+        if status != SA_OK:
+            _check(status)
+        return keep[6]
+
+    return call
+
+
 def prepare_decode(q, k, v, sinks, cu_seqlens_k, max_seqlen_k, kv_chunk_size, sm_scale,
                    workspace, out, lse=None, stream=None):
     """One ``sink_attn_decode`` call with its arguments checked and marshalled once:

@@ -25,6 +25,7 @@
 // K/V tiles are double-buffered: the next tile's global loads are in flight
 // while the current tile is computed.
 #include "common.h"
+#include "decode_tile.h"
 #include "kernels.h"
 
 namespace sa {
@@ -98,7 +99,128 @@ __device__ __forceinline__ float exp_tile(f32x16 (&s)[2], float scale_log2, floa
 // to stage a tile with one 16-byte load each, and the second load spilled registers).
 constexpr int query_blocks(int G) { return G >= 8 ? 1 : (8 % G == 0 ? 8 / G : 16 / G); }
 
-template <int G, bool kSplit, bool kHeadSlices = false>
+// A sequence with at most 16 / G query rows (decode steps, short chunks) in a
+// workgroup of kWaves waves: up to eight waves split the keys of KV head g evenly,
+// each streaming its share the way the split-KV decode does (decode_tile.h: nontemporal
+// loads, two 32-key tiles in flight) for the L_q x G (row, head) columns, and the
+// waves combine their states through LDS.  A 32-row query block per KV head would
+// instead stream every key through one workgroup with one staged tile at a time.
+// It reuses the tile buffers: waves 0-3 keep their V slices, then their state
+// records, in the K buffers (lds_k), waves 4-7 in the V buffers (lds_v).
+constexpr int kShortMaxCols = 16;
+constexpr int kShortWaves = 8;
+constexpr int kShortStateFloats = 2 * kShortMaxCols + kD * kShortMaxCols;  // m, d, acc
+static_assert(4 * kDecodeVSlice <= 2 * kBK * kStride && 4 * kDecodeVSlice <= 2 * kBK * kVStride &&
+                  4 * kShortStateFloats * 2 <= 2 * kBK * kStride,
+              "four waves' V slices and state records fit in each pair of tile buffers");
+
+template <int G, int kWaves>
+__device__ __forceinline__ void short_rows(const uint16_t* __restrict__ q,
+                                           const uint16_t* __restrict__ k,
+                                           const uint16_t* __restrict__ v,
+                                           const float* __restrict__ sinks, int hq, int hkv,
+                                           int g, int q0, int lq, int k0, int lk, int causal,
+                                           float scale_log2, uint16_t* __restrict__ out,
+                                           float* __restrict__ lse, uint16_t* lds_k,
+                                           uint16_t* lds_v) {
+    constexpr int nw = kWaves < kShortWaves ? kWaves : kShortWaves;
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const int q4 = lane / 16, c16 = lane % 16;
+    // column c16 = (row r, head hh); columns past lq * G only pad the MFMA
+    const bool col_ok = c16 < lq * G;
+    const int r = col_ok ? c16 / G : 0, hh = c16 % G;
+    const int h = g * G + hh;
+    // keys row r sees (bottom-right causal alignment); the last row sees all lk
+    const int lim = !col_ok ? 0 : causal ? max(0, min(lk, lk - lq + r + 1)) : lk;
+    // this wave's share of the keys: equal runs of whole 32-key tiles
+    const int per = ceil_div(ceil_div(lk, nw), kDecodeTileKeys) * kDecodeTileKeys;
+    const int lo = min(wave * per, lk);
+    const int hi = wave < nw ? min(lo + per, lk) : lo;
+
+    WaveState st;
+    st.m = (wave == 0 && col_ok) ? sinks[h] * kLog2e : kNegInf;  // the first block holds the sink
+    st.dl = (q4 == 0) ? 1.0f : 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) st.o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 qb0 = {}, qb1 = {};
+    if (col_ok) {
+        const uint16_t* qp = q + ((int64_t)(q0 + r) * hq + h) * kD + 8 * q4;
+        qb0 = load_bf16x8(qp);
+        qb1 = load_bf16x8(qp + 32);
+    }
+    const int row_stride = hkv * kD;
+    const uint16_t* kbase = k + ((int64_t)k0 * hkv + g) * kD;
+    const uint16_t* vbase = v + ((int64_t)k0 * hkv + g) * kD;
+    const int ws = wave < nw ? wave : 0;
+    uint16_t* vw = (ws < 4 ? lds_k : lds_v) + (ws % 4) * kDecodeVSlice;
+    const int ntiles = lo < hi ? ceil_div(hi - lo, kDecodeTileKeys) : 0;
+    if (ntiles > 0) {  // (uniform per wave) see the split-KV decode's loop
+        constexpr int kDepth = 2;
+        DecodeTile buf[kDepth];
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d)
+            load_tile<true>(buf[d], kbase, vbase, row_stride, lo + d * kDecodeTileKeys, hi, lane);
+        int it = 0;
+        do {
+#pragma unroll
+            for (int d = 0; d < kDepth; ++d) {
+                const int ts = lo + (it + d) * kDecodeTileKeys;
+                process_tile(st, buf[d], qb0, qb1, vw, ts, min(lim, hi), scale_log2, lane);
+                load_tile<true>(buf[d], kbase, vbase, row_stride, ts + kDepth * kDecodeTileKeys,
+                                hi, lane);
+            }
+            it += kDepth;
+        } while (it < ntiles);
+    }
+    st.dl += xor16(st.dl);
+    st.dl = sum_xor32(st.dl);
+
+    // combine: wave w's (m, d, acc) of every column into LDS, then one thread per
+    // (column, dimension) output
+    __syncthreads();  // every wave is done with its V slice
+    auto record = [&](int w) {
+        return reinterpret_cast<float*>(w < 4 ? lds_k : lds_v) + (w % 4) * kShortStateFloats;
+    };
+    if (wave < nw) {
+        float* mine = record(wave);
+        if (q4 == 0) {
+            mine[c16] = st.m;
+            mine[kShortMaxCols + c16] = st.dl;
+        }
+        float* acc = mine + 2 * kShortMaxCols;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[(16 * mt + 4 * q4 + i) * kShortMaxCols + c16] = st.o[mt][i];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < lq * G * kD; idx += 64 * kWaves) {
+        const int col = idx / kD, dim = idx % kD;
+        float big = kNegInf;
+#pragma unroll
+        for (int w = 0; w < nw; ++w) big = fmaxf(big, record(w)[col]);
+        float num = 0.0f, den = 0.0f;
+        if (big != kNegInf) {
+#pragma unroll
+            for (int w = 0; w < nw; ++w) {
+                const float* st_w = record(w);
+                const float mw = st_w[col];
+                const float wt = mw == kNegInf ? 0.0f : fast_exp2(mw - big);
+                den += wt * st_w[kShortMaxCols + col];
+                num += wt * st_w[2 * kShortMaxCols + dim * kShortMaxCols + col];
+            }
+        }
+        const bool empty = big == kNegInf || !(den > 0.0f);
+        const int64_t orow = (int64_t)(q0 + col / G) * hq + g * G + col % G;
+        out[orow * kD + dim] = f32_to_bf16_bits(empty ? 0.0f : num / den);
+        if (lse != nullptr && dim == 0) lse[orow] = empty ? kNegInf : (big + fast_log2(den)) * kLn2;
+    }
+}
+
+// kShortRows (unsplit launches whose keys outnumber their queries, G <= 16): the
+// workgroups of sequences with at most 16 / G query rows take the short_rows path,
+// and the first query group of every (sequence, KV head) pair is issued first.
+template <int G, bool kSplit, bool kHeadSlices = false, bool kShortRows = false>
 __global__ __launch_bounds__(64 * G * query_blocks(G)) __attribute__((amdgpu_waves_per_eu(4)))
 void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                   const uint16_t* __restrict__ v, const float* __restrict__ sinks,
@@ -113,6 +235,7 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     constexpr int kPer = (kSegs + kThreads - 1) / kThreads;
     __shared__ uint16_t kl[2][kBK * kStride];
     __shared__ uint16_t vl[2][kBK * kVStride];
+    constexpr bool kShort = kShortRows && !kSplit && !kHeadSlices && G <= kShortMaxCols;
 
     // Work item -> (sequence b, KV head g, group of kQB query blocks qg).  Query
     // blocks go heaviest first (the causal triangle gives late blocks the most keys).
@@ -133,20 +256,37 @@ void prefill_mfma(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k
     const int rest = kSplit ? (int)(blockIdx.x % per_chunk) : (int)blockIdx.x;
     const int hs = kHeadSlices ? rest / per_slice : 0;
     const int bid = kHeadSlices ? rest % per_slice : rest;
+    // kShort: the first query group of every pair goes first (a pair of a decode
+    // step or a short chunk has that one group only, and streams every key of its
+    // sequence), then groups 1 .. n_qgroups - 1 as described.
+    const int lead = kShort ? pairs : 0;
+    const int ng = kShort ? max(n_qgroups - 1, 1) : n_qgroups;
     int pair, qg;
-    if (pairs % 8 == 0) {
-        const int xcd = bid % 8, j = bid / 8, per_xcd = pairs / 8;
-        pair = (pair_major ? j / n_qgroups : j % per_xcd) * 8 + xcd;
-        qg = n_qgroups - 1 - (pair_major ? j % n_qgroups : j / per_xcd);
+    if (kShort && bid < lead) {
+        pair = bid;  // (pair % 8 == bid % 8: the XCD its other groups run on)
+        qg = 0;
+    } else if (pairs % 8 == 0) {
+        const int rb = bid - lead;
+        const int xcd = rb % 8, j = rb / 8, per_xcd = pairs / 8;
+        pair = (pair_major ? j / ng : j % per_xcd) * 8 + xcd;
+        qg = n_qgroups - 1 - (pair_major ? j % ng : j / per_xcd);
     } else {
-        pair = pair_major ? bid / n_qgroups : bid % pairs;
-        qg = n_qgroups - 1 - (pair_major ? bid % n_qgroups : bid / pairs);
+        const int rb = bid - lead;
+        pair = pair_major ? rb / ng : rb % pairs;
+        qg = n_qgroups - 1 - (pair_major ? rb % ng : rb / pairs);
     }
     const int b = pair / hkv, g = pair % hkv;
     const int q0 = cu_q[b], lq = cu_q[b + 1] - q0;
     const int k0 = cu_k[b], lk = cu_k[b + 1] - k0;
     const int r0g = qg * kQB * kBQ;  // first row of the workgroup's query blocks
     if (r0g >= lq) return;           // uniform over the workgroup
+    if constexpr (kShort) {
+        if (lq * G <= kShortMaxCols) {  // uniform: a few query rows
+            short_rows<G, G * kQB>(q, k, v, sinks, hq, hkv, g, q0, lq, k0, lk, causal, scale_log2,
+                                   out, lse, &kl[0][0], &vl[0][0]);
+            return;
+        }
+    }
 
     const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
     const int h = g * group + hs * G + wave % G;
@@ -358,6 +498,11 @@ hipError_t launch_g(const void* q, const void* k, const void* v, const float* si
                            stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                            sinks, cu_q, cu_k, hq, hkv, batch, n_qgroups, pair_major, sm_scale * kLog2e, causal,
                            nullptr, nullptr, ss, part_m, part_d, part_acc);
+    else if (!kHeadSlices && G <= kShortMaxCols && pair_major)
+        hipLaunchKernelGGL((prefill_mfma<G, false, false, true>), dim3((unsigned)blocks), threads, 0,
+                           stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                           sinks, cu_q, cu_k, hq, hkv, batch, n_qgroups, pair_major, sm_scale * kLog2e, causal,
+                           (uint16_t*)out, lse, ss, nullptr, nullptr, nullptr);
     else
         hipLaunchKernelGGL((prefill_mfma<G, false, kHeadSlices>), dim3((unsigned)blocks), threads, 0,
                            stream, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,

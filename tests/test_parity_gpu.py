@@ -599,3 +599,26 @@ def test_random_configurations(orc, seed):
     dout, dlse = H.run_decode_call(dev, int(rng.integers(1, 200)), q=qd)
     H.assert_close(dout, ref[last], bf16=bf16)
     H.assert_lse_close(dlse, ref_lse[last], bf16=bf16)
+
+
+# ---------------------------------------------------------------- short query rows in prefill
+
+@pytest.mark.parametrize("group", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_short_query_rows(orc, group, causal):
+    """Sequences of at most 16 / G query rows (the prefill call's decode-style path: the
+    workgroup's waves split the keys and combine their states in LDS), mixed with longer
+    chunks in one call, over caches from 0 to 9000 keys; every output element."""
+    rows = max(1, 16 // group)
+    lq = [1, rows, rows, 1, 40, rows, 1]
+    lk = [5000, rows + 9000, rows, 1, 700, rows + 37, 0 if not causal else 1]
+    hkv = 2
+    wl = W.make_workload(f"short_rows_g{group}", dtype="bf16", kind="prefill", seqlens_q=lq,
+                         seqlens_k=lk, num_q_heads=hkv * group, num_kv_heads=hkv, head_dim=64,
+                         seed=900 + group, causal=causal,
+                         sink_values=([-np.inf, 20.0, -20.0, 0.5, 3.0] * group)[:hkv * group])
+    dev = H.Device(wl)
+    out, lse = H.run_prefill(dev)
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    H.assert_close(out, ref, bf16=True)
+    H.assert_lse_close(lse, ref_lse, bf16=True)

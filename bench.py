@@ -472,7 +472,7 @@ def bench_ragged_decode(steps: int = 40, warmup: int = 20):
 MIXED_COPIES = 4  # rotated copies of the mixed batch's K/V (4 x 332 MB)
 
 
-def bench_mixed_varlen(steps: int = 40, warmup: int = 20):
+def bench_mixed_varlen(steps: int = 40, warmup: int = 20, side=None):
     """The mixed packed batch (4 prefill chunks of 512-2048 new tokens over 0-8192 cached
     keys, then 12 single-token decodes over 1024-32768 keys, 64/8 heads, bf16).  Each part
     against its own roofline: the prefill chunks in one prefill call (TFLOP/s over their
@@ -522,7 +522,8 @@ def bench_mixed_varlen(steps: int = 40, warmup: int = 20):
                                    wl.sm_scale, ws_fixed, out_dec) for j in range(MIXED_COPIES)]
     one = [sa.prepare_prefill(q, ks[j], vs[j], sinks, cu_q, cu_k, int(lq.max()), int(lk.max()),
                               wl.sm_scale, out) for j in range(MIXED_COPIES)]
-    side = torch.cuda.Stream(device=dev)  # default priority
+    if side is None:
+        side = torch.cuda.Stream(device=dev)  # default priority
     side_dec = []
     with torch.cuda.stream(side):
         side_dec = [sa.prepare_decode(q_dec, ks[j], vs[j], sinks, cu_dec, max_k_dec, 0,
@@ -830,10 +831,19 @@ def main(argv=None):
         return 1
     torch.cuda.set_device(0)
 
-    # The mixed batch runs first: after the decode section (its graph captures and
-    # host-synchronised loops) its two streams no longer overlap in this process.
-    mixed = None if args.no_prefill else bench_mixed_varlen()
+    # HIP binds a stream to one of the process's hardware queues (GPU_MAX_HW_QUEUES,
+    # 4 by default) round-robin when the stream first submits work, and kernels on
+    # one hardware queue run in order.  The mixed batch's second stream therefore gets
+    # its first work here, right after the default stream's, so that the two land on
+    # different queues whatever the later legs create (a side stream first used after
+    # the decode section's graph-capture streams shared the default stream's queue).
+    torch.zeros(1, device="cuda").add_(1)
+    side = torch.cuda.Stream()  # default priority
+    with torch.cuda.stream(side):
+        torch.zeros(1, device="cuda").add_(1)
+    torch.cuda.synchronize()
     dec = bench_decode(args.steps, args.warmup)
+    mixed = None if args.no_prefill else bench_mixed_varlen(side=side)
     tiny = None if args.no_prefill else bench_tiny_prefill()
     pre = None if args.no_prefill else bench_prefill(args.prefill_steps, 50)
     long_kv = None if args.no_prefill else bench_prefill_long_kv(max(10, args.prefill_steps // 2), 20)

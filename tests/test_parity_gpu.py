@@ -395,6 +395,40 @@ def run_prefill_split(dev: "H.Device", chunk: int, causal=None):
     return pm, pd, pa, out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_prefill_split_spare_chunk_slots(orc, dtype):
+    """max_num_chunks three above what the keys need: the slots past each sequence's
+    last chunk hold the empty state (m = -inf, d = 0, acc = 0), every slot merges to the
+    plain definition, and decode split + merge with spare slots does too."""
+    bf16 = dtype == "bf16"
+    wl = W.random_case(140, dtype=dtype, batch=3, hq=16, hkv=2, max_q=90, max_k=700,
+                       sink_values=[-np.inf, 20.0, -20.0, 0.5] * 4)
+    dev = H.Device(wl)
+    chunk = 128
+    need = -(-dev.max_lk // chunk)
+    pm, pd, pa = sa.prefill_split(dev.q, dev.k, dev.v, dev.sinks, dev.cu_q, dev.cu_k,
+                                  dev.max_lq, dev.max_lk, chunk, wl.sm_scale, causal=True,
+                                  max_num_chunks=need + 3)
+    out, lse = sa.merge_rows(pm, pd, pa, out_dtype=dev.dtype, return_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
+    H.assert_close(out.float().cpu().numpy().astype(np.float64), ref, bf16=bf16)
+    H.assert_lse_close(lse.cpu().numpy().astype(np.float64), ref_lse, bf16=bf16)
+    pm, pd, pa = pm.cpu().numpy(), pd.cpu().numpy(), pa.cpu().numpy()
+    for b in range(wl.batch):
+        rows = slice(int(wl.cu_q[b]), int(wl.cu_q[b + 1]))
+        first_spare = max(1, -(-int(wl.seqlens_k[b]) // chunk))
+        assert np.all(pm[rows, :, first_spare:] == -np.inf)
+        assert np.all(pd[rows, :, first_spare:] == 0.0)
+        assert np.all(pa[rows, :, first_spare:, :] == 0.0)
+    # the one-call decode with spare chunk slots (each sequence's last query row)
+    last = (wl.cu_q[1:] - 1).astype(np.int64)
+    qd = dev.q[torch.from_numpy(last).cuda()].contiguous()
+    dout, dlse = H.run_decode_call(dev, chunk, q=qd, max_num_chunks=need + 3)
+    H.assert_close(dout, ref[last], bf16=bf16)
+    H.assert_lse_close(dlse, ref_lse[last], bf16=bf16)
+
+
 @pytest.mark.parametrize("group", [1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 17, 24, 32, 64])
 @pytest.mark.parametrize("chunk", [64, 100, 1024])
 @pytest.mark.parametrize("causal", [True, False])

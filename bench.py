@@ -171,9 +171,12 @@ def bench_decode(steps: int, warmup: int):
 
 
 def bench_tiny_prefill(steps: int = 400):
-    """The tiny fp32 causal prefill (1 x 128 tokens, 4 query heads on 1 KV head): launch
-    latency bound, so its time is reported two ways: back-to-back calls (GPU time per
-    call, from an event pair) and one call at a time with the host waiting for each."""
+    """The tiny fp32 causal prefill (1 x 128 tokens, 4 query heads on 1 KV head), timed two
+    ways: back-to-back calls (GPU time per call, from an event pair) and one call at a time
+    with the host waiting for each.  The fp32 kernel gives four lanes to each (row, head)
+    pair, so this size runs 32 workgroups of 64 lanes, each streaming up to four 32-key
+    tiles through LDS one after another: the call is bound by that short chain, not by
+    the launch."""
     import torch
     import gqa_attention_head_amd as sa
     from gqa_attention_head_amd import workloads as W
@@ -205,7 +208,7 @@ def bench_tiny_prefill(steps: int = 400):
     return {"workload": "tiny_prefill_fp32_b1_s128_hq4_hkv1_d64", "dtype": "f32",
             "ms_back_to_back": round(gpu_ms, 5), "ms_host_synced": round(synced_ms, 5),
             "flops": wl.prefill_flops(),
-            "note": "launch-latency bound: time only; parity is checked in the CPU baseline leg and the tests",
+            "note": "fp32 vector-ALU kernel, 32 workgroups at this size (four lanes per row and head): time only; parity is checked in the CPU baseline leg and the tests",
             "_out": out.cpu().numpy(), "_wl": wl}
 
 
@@ -783,8 +786,10 @@ def _cpu_epilogue():
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "traffic_decode_b32_kv4096_prefill_b4_s4096.md")
 TRAFFIC_SOURCES = {
-    "decode": ("gqa_attention_head_amd/csrc/common.h", "gqa_attention_head_amd/csrc/decode.hip"),
-    "prefill": ("gqa_attention_head_amd/csrc/common.h", "gqa_attention_head_amd/csrc/prefill.hip"),
+    "decode": ("gqa_attention_head_amd/csrc/common.h", "gqa_attention_head_amd/csrc/decode_tile.h",
+               "gqa_attention_head_amd/csrc/decode.hip"),
+    "prefill": ("gqa_attention_head_amd/csrc/common.h", "gqa_attention_head_amd/csrc/decode_tile.h",
+                "gqa_attention_head_amd/csrc/prefill.hip"),
     "router": ("gqa_attention_head_amd/csrc/common.h", "gqa_attention_head_amd/csrc/router.hip"),
     "epilogue": ("gqa_attention_head_amd/csrc/common.h", "gqa_attention_head_amd/csrc/epilogue.hip"),
 }

@@ -275,3 +275,25 @@ def test_epilogue_rejects_mis_shaped(no_library, case):
         kw["q"] = host(3, 7, 64)
     with pytest.raises(ValueError):
         sa.qkv_bias_rope(args["qkv"], args["bias"], args["positions"], args["cos_sin"], 8, 2, **kw)
+
+
+def test_prepared_calls_and_noalloc_reject_mis_shaped(no_library):
+    """prepare_prefill, prepare_decode and decode_noalloc run the same checks before any
+    library call."""
+    q, k, v, s = _qkv()
+    cq, ck = _cu(0, 2, 6), _cu(0, 4, 10)
+    with pytest.raises(ValueError):  # sinks of the wrong length
+        sa.prepare_prefill(q, k, v, host(7, dtype=torch.float32), cq, ck, 4, 6, 0.125,
+                           host(6, 8, 64))
+    with pytest.raises(ValueError):  # out of the wrong head dim
+        sa.prepare_prefill(q, k, v, s, cq, ck, 4, 6, 0.125, host(6, 8, 32))
+    q, k, v, s = _qkv(tq=2)
+    cu = _cu(0, 4, 10)
+    with pytest.raises(ValueError):  # out of the wrong head dim
+        sa.prepare_decode(q, k, v, s, cu, 6, 2, 0.125, _Workspace(2, 8, 3), host(2, 8, 32))
+    with pytest.raises(ValueError):  # workspace for another batch
+        sa.prepare_decode(q, k, v, s, cu, 6, 2, 0.125, _Workspace(3, 8, 3), host(2, 8, 64))
+    with pytest.raises(ValueError):  # cu_seqlens_k for another batch
+        sa.decode_noalloc(q, k, v, s, _cu(0, 4, 10, 12), 6, 0.125)
+    with pytest.raises(ValueError):  # lse of the wrong shape
+        sa.decode_noalloc(q, k, v, s, cu, 6, 0.125, lse=host(2, 9, dtype=torch.float32))

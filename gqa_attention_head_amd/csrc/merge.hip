@@ -12,8 +12,8 @@
 // are combined from one round trip: lane c reads block c's m and d, every lane
 // reads its dimension of each block's accumulator (all of those loads issued
 // before any is used, in groups of kGroup rows), and the maximum and the weighted
-// scale sum are wave reductions.  Past 64 blocks, further rounds of 64 fold in
-// with the usual rescale of the running sums.  The first round's loads go out
+// scale sum are wave reductions.  Past 64 blocks, further passes of 64 fold in
+// with the usual rescale of the running sums.  The first pass's loads go out
 // before the sequence's block count is known (slots clamped to the buffer and
 // masked afterwards).
 #include "common.h"
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void merge_kernel(
     const int64_t s0 = b * lay.seq + h * lay.head;  // slot of block 0
     auto slot = [&](int c) { return s0 + (int64_t)min(c, nc - 1) * lay.block; };
 
-    // round 0, before the block count is known: m and d of blocks 0..63 (lane = block)
+    // first pass, before the block count is known: m and d of blocks 0..63 (lane = block)
     // and the first group of accumulator rows
     float m_ld = part_m[slot(lane)];
     float d_ld = part_d[slot(lane)];
@@ -87,10 +87,10 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void merge_kernel(
     }
 
     float big = kNegInf, acc = 0.0f, den = 0.0f;
-    for (int r0 = 0;;) {  // rounds of up to 64 blocks
+    for (int r0 = 0;;) {  // passes of up to 64 blocks
         const int nr = min(nch - r0, 64);
         const int groups = ceil_div(nr, kGroup);
-        // the rest of this round's accumulator rows, every load before any use
+        // the rest of this pass's accumulator rows, every load before any use
         if (r0 > 0) {
 #pragma unroll
             for (int u = 0; u < kGroup; ++u) a[0][u] = part_acc[slot(r0 + u) * kD + lane];
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void merge_kernel(
         const bool mine = lane < nr;
         const float ml = mine ? m_ld : kNegInf;
         const float rbig = wave_reduce<true>(ml);
-        if (rbig != kNegInf) {  // (uniform) some block of the round holds mass
+        if (rbig != kNegInf) {  // (uniform) some block of the pass holds mass
             const float nb = fmaxf(big, rbig);
             if (big != kNegInf && nb != big) {
                 const float sc = fast_exp2((big - nb) * kLog2e);

@@ -174,9 +174,9 @@ def bench_tiny_prefill(steps: int = 400):
     """The tiny fp32 causal prefill (1 x 128 tokens, 4 query heads on 1 KV head), timed two
     ways: back-to-back calls (GPU time per call, from an event pair) and one call at a time
     with the host waiting for each.  The fp32 kernel gives four lanes to each (row, head)
-    pair, so this size runs 32 workgroups of 64 lanes, each streaming up to four 32-key
-    tiles through LDS one after another: the call is bound by that short chain, not by
-    the launch."""
+    pair, so this size runs 32 workgroups of 64 lanes, each walking up to four 32-key
+    tiles one after another (the next tile's loads in flight while one is used): the call
+    is bound by that short chain, not by the launch."""
     import torch
     import gqa_attention_head_amd as sa
     from gqa_attention_head_amd import workloads as W

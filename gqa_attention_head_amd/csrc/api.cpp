@@ -134,6 +134,20 @@ sa_status_t check_chunk_span(int32_t kv_chunk_size, int32_t max_num_chunks, cons
     return SA_OK;
 }
 
+// The kernels move q, k, v and the accumulator states in 16-byte pieces and a prefill
+// output row in 8-byte pieces: those pointers must be aligned to match.
+bool aligned(const void* p, uintptr_t bytes) {
+    return p == nullptr || (reinterpret_cast<uintptr_t>(p) % bytes) == 0;
+}
+sa_status_t check_alignment(const char* what, const void* q, const void* k, const void* v,
+                            const void* part_acc, const void* out, uintptr_t out_bytes) {
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(part_acc, 16))
+        return fail(SA_EINVAL, "%s: q, k, v and part_acc must be 16-byte aligned", what);
+    if (!aligned(out, out_bytes))
+        return fail(SA_EINVAL, "%s: out must be %u-byte aligned", what, (unsigned)out_bytes);
+    return SA_OK;
+}
+
 sa_status_t check_dtype(sa_dtype_t d) {
     if (d != SA_FP32 && d != SA_BF16) return fail(SA_EINVAL, "unknown dtype %d", (int)d);
     return SA_OK;
@@ -155,6 +169,7 @@ sa_status_t sink_attn_prefill(sa_dtype_t dtype, const void* q, const void* k, co
     if ((s = check_dtype(dtype)) != SA_OK) return s;
     if (!q || !k || !v || !sinks || !cu_seqlens_q || !cu_seqlens_k || !out)
         return fail(SA_EINVAL, "sink_attn_prefill: null pointer argument");
+    if ((s = check_alignment("sink_attn_prefill", q, k, v, nullptr, out, 8)) != SA_OK) return s;
     if ((s = check_heads(batch, num_q_heads, num_kv_heads, head_dim)) != SA_OK) return s;
     if (max_seqlen_q < 0 || max_seqlen_k < 0)
         return fail(SA_EINVAL, "max_seqlen_q/max_seqlen_k must be >= 0");
@@ -196,6 +211,8 @@ sa_status_t sink_attn_prefill_split(sa_dtype_t dtype, const void* q, const void*
     if (!q || !k || !v || !sinks || !cu_seqlens_q || !cu_seqlens_k || !part_m || !part_d ||
         !part_acc)
         return fail(SA_EINVAL, "sink_attn_prefill_split: null pointer argument");
+    if ((s = check_alignment("sink_attn_prefill_split", q, k, v, part_acc, nullptr, 1)) != SA_OK)
+        return s;
     if ((s = check_heads(batch, num_q_heads, num_kv_heads, head_dim)) != SA_OK) return s;
     if (max_seqlen_q < 0 || max_seqlen_k < 0)
         return fail(SA_EINVAL, "max_seqlen_q/max_seqlen_k must be >= 0");
@@ -251,6 +268,8 @@ sa_status_t sink_attn_prefill_state(sa_dtype_t dtype, const void* q, const void*
     if (!q || !k || !v || !sinks || !cu_seqlens_q || !cu_seqlens_k || !part_m || !part_d ||
         !part_acc)
         return fail(SA_EINVAL, "sink_attn_prefill_state: null pointer argument");
+    if ((s = check_alignment("sink_attn_prefill_state", q, k, v, part_acc, nullptr, 1)) != SA_OK)
+        return s;
     if ((s = check_heads(batch, num_q_heads, num_kv_heads, head_dim)) != SA_OK) return s;
     if (max_seqlen_q < 0 || max_seqlen_k < 0)
         return fail(SA_EINVAL, "max_seqlen_q/max_seqlen_k must be >= 0");
@@ -326,6 +345,7 @@ sa_status_t check_split_args(sa_dtype_t dtype, const void* q, const void* k, con
     if ((s = check_dtype(dtype)) != SA_OK) return s;
     if (!q || !k || !v || !sinks || !cu_seqlens_k || !part_m || !part_d || !part_acc)
         return fail(SA_EINVAL, "decode: null pointer argument");
+    if ((s = check_alignment("decode", q, k, v, part_acc, nullptr, 1)) != SA_OK) return s;
     if ((s = check_heads(batch, num_q_heads, num_kv_heads, head_dim)) != SA_OK) return s;
     if (kv_chunk_size < 0 || (kv_chunk_size == 0 && !allow_balanced))
         return fail(SA_EINVAL, "kv_chunk_size must be >= %d, got %d", allow_balanced ? 0 : 1, kv_chunk_size);
@@ -468,6 +488,8 @@ sa_status_t sink_attn_decode_noalloc(sa_dtype_t dtype, const void* q, const void
     if ((s = check_dtype(dtype)) != SA_OK) return s;
     if (!q || !k || !v || !sinks || !cu_seqlens_k || !out)
         return fail(SA_EINVAL, "sink_attn_decode_noalloc: null pointer argument");
+    if ((s = check_alignment("sink_attn_decode_noalloc", q, k, v, nullptr, nullptr, 1)) != SA_OK)
+        return s;
     if ((s = check_heads(batch, num_q_heads, num_kv_heads, head_dim)) != SA_OK) return s;
     if (max_seqlen_k < 0) return fail(SA_EINVAL, "max_seqlen_k must be >= 0");
     if (!(std::isfinite(sm_scale) && sm_scale > 0.0f))

@@ -25,6 +25,19 @@ __device__ __forceinline__ float to_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) { return bf16_bits_to_f32(x); }
 
+// Element e of a 16-byte piece, widened to fp32.
+template <typename T>
+__device__ __forceinline__ float piece_elem(const u32x4& w, int e);
+template <>
+__device__ __forceinline__ float piece_elem<float>(const u32x4& w, int e) {
+    return __uint_as_float(w[e]);
+}
+template <>
+__device__ __forceinline__ float piece_elem<uint16_t>(const u32x4& w, int e) {
+    const uint32_t word = w[e / 2];
+    return bf16_bits_to_f32(static_cast<uint16_t>(e % 2 == 0 ? word & 0xFFFFu : word >> 16));
+}
+
 template <typename T>
 __device__ __forceinline__ T from_f32(float x);
 template <>
@@ -124,16 +137,43 @@ __global__ __launch_bounds__(64) void rows_kernel(
 #pragma unroll
     for (int d = 0; d < kDL; ++d) acc[d] = 0.0f;
 
-    for (int t0 = key_lo; t0 < key_hi; t0 += kTileKeys) {
-        __syncthreads();
-        for (int idx = lane; idx < kTileKeys * kD; idx += 64) {
-            const int j = idx / kD, d = idx % kD;
-            const int key = min(t0 + j, key_hi - 1);
-            const int64_t off = ((int64_t)(k0 + key) * hkv + g) * kD + d;
-            ks[j][d] = to_f32<T>(k[off]);
-            vs[j][d] = to_f32<T>(v[off]);
+    // K/V tiles move in 16-byte pieces (4 fp32 or 8 bf16 elements): each lane loads
+    // kPieces of each into registers, the next tile's while the current one is used,
+    // and widens them to fp32 in LDS.
+    constexpr int kPieceElems = 16 / sizeof(T);
+    constexpr int kPiecesPerRow = kD / kPieceElems;
+    constexpr int kPieces = kTileKeys * kPiecesPerRow / 64;  // per lane, K and V each
+    u32x4 kr[kPieces], vr[kPieces];
+    auto gload = [&](int t0) {
+#pragma unroll
+        for (int p = 0; p < kPieces; ++p) {
+            const int piece = lane + 64 * p;
+            const int key = min(t0 + piece / kPiecesPerRow, key_hi - 1);
+            const int64_t off =
+                ((int64_t)(k0 + key) * hkv + g) * kD + (piece % kPiecesPerRow) * kPieceElems;
+            kr[p] = *reinterpret_cast<const u32x4*>(k + off);
+            vr[p] = *reinterpret_cast<const u32x4*>(v + off);
         }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int p = 0; p < kPieces; ++p) {
+            const int piece = lane + 64 * p;
+            const int j = piece / kPiecesPerRow, d = (piece % kPiecesPerRow) * kPieceElems;
+#pragma unroll
+            for (int e = 0; e < kPieceElems; ++e) {
+                ks[j][d + e] = piece_elem<T>(kr[p], e);
+                vs[j][d + e] = piece_elem<T>(vr[p], e);
+            }
+        }
+    };
+    if (key_lo < key_hi) gload(key_lo);
+
+    for (int t0 = key_lo; t0 < key_hi; t0 += kTileKeys) {
+        __syncthreads();  // every lane is done with the previous tile
+        lstore();
         __syncthreads();
+        if (t0 + kTileKeys < key_hi) gload(t0 + kTileKeys);
         float s[kTileKeys];
         float tmax = kNegInf;
 #pragma unroll

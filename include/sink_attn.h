@@ -38,6 +38,10 @@
  *     of the last error of the calling thread is returned by
  *     sink_attn_last_error().
  *   - sm_scale must be finite and > 0 (SA_EINVAL otherwise).
+ *   - Alignment: q, k, v and part_acc must be 16-byte aligned, and the out of
+ *     sink_attn_prefill 8-byte aligned (the kernels move them in pieces of that
+ *     size); SA_EINVAL otherwise.  Allocations from hipMalloc (or torch) and
+ *     row-offset views of them meet this.
  *   - Device-resident preconditions cannot be checked without a
  *     synchronisation and are the caller's duty: monotone cu_seqlens,
  *     L_q <= L_k for every sequence under causal masking, per-sequence

@@ -81,3 +81,64 @@ def test_captured_sequence_replays_bit_for_bit():
                                want.view(torch.uint8) if want.dtype == torch.bfloat16 else want), \
                 f"replay {i}: {name} differs"
         _ = (torch.randn(4096, device="cuda") * 3).sum().item()  # eager work in between
+
+
+def _decode_inputs(seed, batch, max_k):
+    wl = W.random_case(seed, batch=batch, hq=64, hkv=8, max_k=max_k, decode=True)
+    q, k, v = (bf16_dev(a) for a in wl.device_arrays())
+    return (wl, q, k, v, torch.from_numpy(wl.sinks).cuda(), torch.from_numpy(wl.cu_k).cuda(),
+            int(wl.seqlens_k.max()))
+
+
+def _replays_equal(graph, outs, eager, scribble):
+    """Replay three times, with eager work and a synchronisation in between, after
+    the outputs are cleared; every replay must equal the eager result bit for bit."""
+    for t in outs:
+        t.zero_()
+    for _ in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outs, eager):
+            a = got.view(torch.uint8) if got.dtype == torch.bfloat16 else got
+            b = want.view(torch.uint8) if want.dtype == torch.bfloat16 else want
+            assert torch.equal(a, b)
+        scribble()
+        torch.cuda.synchronize()
+
+
+def test_captured_proportional_decode_replays_bit_for_bit():
+    """DecodeGraph over the proportional-block decode (kv_chunk_size 0)."""
+    wl, q, k, v, sinks, cu, max_k = _decode_inputs(41, 11, 20000)
+    out = torch.empty(wl.batch, 64, 64, device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty(wl.batch, 64, device="cuda")
+    ws = sa.DecodeWorkspace(wl.batch, 64, sa.balanced_slots(wl.batch, 64, 64))
+    e_out, e_lse = sa.decode(q, k, v, sinks, cu, max_k, 0, wl.sm_scale, workspace=ws,
+                             return_lse=True)
+    torch.cuda.synchronize()
+    g = sa.DecodeGraph(q, k, v, sinks, cu, max_k, 0, wl.sm_scale, out=out, lse=lse)
+    junk = torch.empty(1 << 20, device="cuda")
+    _replays_equal(g, (out, lse), (e_out, e_lse), lambda: junk.normal_())
+
+
+def test_captured_noalloc_decode_replays_bit_for_bit():
+    """The allocation-free decode captured in a graph: its states live in the library's
+    fixed array, so the captured launches need no caller workspace at all."""
+    wl, q, k, v, sinks, cu, max_k = _decode_inputs(42, 13, 30000)
+    out = torch.empty(wl.batch, 64, 64, device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty(wl.batch, 64, device="cuda")
+    sa.decode_noalloc(q, k, v, sinks, cu, max_k, wl.sm_scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    eager = (out.clone(), lse.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sa.decode_noalloc(q, k, v, sinks, cu, max_k, wl.sm_scale, out=out, lse=lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sa.decode_noalloc(q, k, v, sinks, cu, max_k, wl.sm_scale, out=out, lse=lse)
+    # eager work between replays that also uses the library's state array
+    other = _decode_inputs(43, 5, 9000)
+    _replays_equal(graph, (out, lse), eager,
+                   lambda: sa.decode_noalloc(*other[1:6], other[6], other[0].sm_scale))

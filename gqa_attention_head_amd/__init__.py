@@ -397,8 +397,9 @@ def decode(q, k, v, sinks, cu_seqlens_k, max_seqlen_k, kv_chunk_size, sm_scale,
            stream=None):
     """Split-KV decode in one call (``sink_attn_decode``): split pass then merge, enqueued
     back to back on the stream.  kv_chunk_size > 0 cuts every sequence into chunks of that
-    many keys; kv_chunk_size = 0 lets the library cut the batch's keys into balanced
-    ranges (one per compute unit), using up to max_num_chunks state slots per sequence."""
+    many keys; kv_chunk_size = 0 lets the library cut each sequence into blocks proportional
+    to its length (about one workgroup per compute unit in all), using up to max_num_chunks
+    state slots per sequence."""
     torch = _torch()
     _check_qkv(q, k, v, sinks)
     _check_cu(cu_seqlens_k, "cu_seqlens_k")

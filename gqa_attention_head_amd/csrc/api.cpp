@@ -334,7 +334,7 @@ sa_status_t sink_attn_merge_rows(sa_dtype_t out_dtype, const float* part_m, cons
 
 namespace {
 
-// kv_chunk_size == 0 (balanced ranges) is valid only where allow_balanced is set.
+// kv_chunk_size == 0 (proportional blocks) is valid only where allow_balanced is set.
 sa_status_t check_split_args(sa_dtype_t dtype, const void* q, const void* k, const void* v,
                              const float* sinks, const int32_t* cu_seqlens_k, int32_t batch,
                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,

@@ -98,7 +98,7 @@ bool mfma_decode_supported(int group);
 // Workgroups per key range of the matrix-core decode (blocks of eight waves, one
 // wave per KV head or per slice of its query heads).
 int mfma_decode_head_blocks(int hq, int hkv);
-// Split pass of a one-call decode under `plan` (fixed chunks or balanced ranges).
+// Split pass of a one-call decode under `plan` (fixed chunks or proportional blocks).
 hipError_t launch_mfma_decode_plan(const void* q, const void* k, const void* v,
                                    const float* sinks, const int32_t* cu_k, int batch, int hq,
                                    int hkv, const DecodePlan& plan, float sm_scale,

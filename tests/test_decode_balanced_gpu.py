@@ -1,6 +1,6 @@
-"""GPU parity of the one-call decode with balanced ranges (``sink_attn_decode`` with
-kv_chunk_size = 0): the batch's keys are cut into equal ranges, one per compute
-unit, whatever the sequence lengths.  Each case is compared element by element
+"""GPU parity of the one-call decode with proportional blocks (``sink_attn_decode`` with
+kv_chunk_size = 0): each sequence is cut into a number of blocks proportional to its
+length, about one workgroup per compute unit in all, whatever the sequence lengths.  Each case is compared element by element
 with the fp64 oracle; the partial-state buffers sit between NaN guard bands that
 must stay untouched."""
 from __future__ import annotations
@@ -47,7 +47,7 @@ class GuardedWorkspace:
 
 
 def balanced(dev, q=None, cu_k=None, max_lk=None, slots=None, chunk=0, calls=1):
-    """sink_attn_decode with balanced ranges (chunk 0) into a guarded workspace."""
+    """sink_attn_decode with proportional blocks (chunk 0) into a guarded workspace."""
     wl = dev.wl
     q = dev.q if q is None else q
     cu_k = dev.cu_k if cu_k is None else cu_k
@@ -70,7 +70,7 @@ def check(res, ref, ref_lse, bf16=True):
 
 
 def test_balanced_batched_decode(orc):
-    """The 32 x 4096 decode: balanced ranges give the same result as the 8 chunks."""
+    """The 32 x 4096 decode: proportional blocks give the same result as the 8 chunks."""
     wl = W.workload(2)
     dev = H.Device(wl)
     ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
@@ -104,9 +104,9 @@ def test_balanced_mixed_varlen_decodes(orc):
     [0, 1, 0, 70],                      # empty sequences between others
     [0, 0, 1],                          # almost no keys
     [5000, 0],                          # empty last sequence
-    [0, 3000, 1, 1, 2, 4000],           # a range crossing several sequences
-    [1] * 300,                          # every range spans many sequences
-    [129, 127, 128, 256, 255, 257],     # around the minimum range length
+    [0, 3000, 1, 1, 2, 4000],           # long and one-key sequences side by side
+    [1] * 300,                          # more sequences than block columns
+    [129, 127, 128, 256, 255, 257],     # around the 32- and 64-key tile sizes
 ])
 def test_balanced_empty_and_short_sequences(orc, lengths):
     wl = W.make_workload("balanced_edges", dtype="bf16", kind="decode",
@@ -132,8 +132,8 @@ def test_balanced_group_sizes(orc, group):
 
 @pytest.mark.parametrize("slots", [2, 3, 5, 1])
 def test_balanced_few_slots(orc, slots):
-    """Few state slots per sequence: the ranges grow so that no sequence meets more
-    ranges than there are slots (one slot: one block per sequence)."""
+    """Few state slots per sequence: the blocks grow so that no sequence gets more
+    blocks than there are slots (one slot: one block per sequence)."""
     wl = W.random_case(350 + slots, batch=6, hq=16, hkv=2, max_k=9000, decode=True)
     dev = H.Device(wl)
     ref, ref_lse = orc.workload(wl, nthreads=NTHREADS)
@@ -170,7 +170,7 @@ def test_balanced_many_short_sequences(orc):
 
 
 def test_balanced_max_batch(orc):
-    """65535 sequences of 1-3 keys: the range-to-sequence search over the largest batch
+    """65535 sequences of 1-3 keys: the block-to-sequence search over the largest batch
     (three narrowing rounds), sampled sequences against the oracle."""
     batch = 65535
     rng = np.random.default_rng(83)
@@ -189,7 +189,7 @@ def test_balanced_max_batch(orc):
 
 
 def test_balanced_matches_fixed_chunks():
-    """Balanced ranges and fixed chunks agree with each other to the bf16 output's
+    """Proportional blocks and fixed chunks agree with each other to the bf16 output's
     rounding on the ragged long decode."""
     wl = W.workload(4)
     dev = H.Device(wl)
